@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs, shared by the GPU tests, the bench and the oracle.
+
+This module holds no attention arithmetic: it only draws random numbers,
+casts them to the storage dtype the library consumes, and (for the fp8 path)
+quantises them with a per-tensor descale.  Both sides of every parity check
+read their inputs from here; the oracle then decodes the exact stored values
+to float64 on its own.
+
+Recipe (every workload):
+  * generator ``numpy.random.default_rng(seed)`` (PCG64), seed 0 unless told
+    otherwise; ``standard_normal`` in float64, drawn in the order Q, K, V,
+    each as one full C-ordered tensor of shape (B, H, N, D);
+  * an optional multiplier (0.5 for the large-head-dim workloads), applied in
+    float64 before the cast;
+  * cast to the storage dtype with round-to-nearest-even (torch's cast).
+
+The fp8 recipe draws Q, K, V the same way, then for each tensor in the order
+Q, K, V multiplies round(0.01 * H * D) distinct (head, channel) columns by 8
+(the "1% outlier channels" of the diffusion-style fp8 workload; a channel is
+read as one of the H*D hidden features), then quantises each tensor with
+descale = absmax / 448 (float32) and code = e4m3fn(clamp(x / descale)).
+
+These Gaussian tensors stand in for the captured model activations that the
+ZYFA article measures on (section "What the numbers establish, and where they
+overstate"); the article notes that Gaussian inputs overstate speed-ups.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+E4M3FN_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, dtype and input recipe."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+    causal: bool
+    dtype: str  # "f32", "bf16" or "fp8"
+    value_scale: float = 1.0
+    seed: int = 0
+    outlier_frac: float = 0.0
+    outlier_mult: float = 8.0
+    extra: dict = field(default_factory=dict, compare=False, hash=False)
+
+    @property
+    def scale(self):
+        """Softmax scale 1/sqrt(D) (every workload states or implies it)."""
+        return 1.0 / float(np.sqrt(self.D))
+
+    @property
+    def visible_pairs(self):
+        """Number of visible (query, key) pairs per head."""
+        if not self.causal:
+            return self.Nq * self.Nkv
+        off = self.Nkv - self.Nq
+        total = 0
+        # rows i see keys j <= i + off, clipped to [0, Nkv)
+        lo = max(0, -off)
+        for_rows = np.arange(lo, self.Nq, dtype=np.int64)
+        total = int(np.minimum(for_rows + off + 1, self.Nkv).sum())
+        return total
+
+    @property
+    def flops(self):
+        """Matmul flops: 4 * B * Hq * D * visible pairs (QK^T and PV)."""
+        return 4 * self.B * self.Hq * self.D * self.visible_pairs
+
+    def replace(self, **kw):
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    # tiny fp32 self-attention; the oracle finishes it in well under a second
+    "tiny_f32": Workload("tiny_f32", 1, 2, 2, 256, 256, 64, False, "f32"),
+    # LLM prefill, causal self-attention, bf16
+    "prefill_causal_bf16": Workload("prefill_causal_bf16", 4, 32, 32, 4096, 4096, 128, True, "bf16"),
+    # GQA causal prefill (group size 4) and its cross-attention variant
+    "gqa_causal_bf16": Workload("gqa_causal_bf16", 2, 32, 8, 8192, 8192, 128, True, "bf16"),
+    "gqa_cross_bf16": Workload("gqa_cross_bf16", 2, 32, 8, 2048, 8192, 128, False, "bf16"),
+    # large head dims (split-D), inputs scaled by 0.5
+    **{
+        f"splitd_bf16_d{d}": Workload(f"splitd_bf16_d{d}", 1, 8, 8, 4096, 4096, d, False, "bf16", value_scale=0.5)
+        for d in (320, 512, 768, 1024)
+    },
+    # fp8 e4m3 diffusion-style attention with 1% outlier channels
+    "fp8_outlier": Workload("fp8_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01),
+}
+
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def draw_gaussian_qkv(w: Workload):
+    """float64 numpy Q, K, V drawn in that order from the workload's seed."""
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal((w.B, w.Hq, w.Nq, w.D))
+    k = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.D))
+    v = rng.standard_normal((w.B, w.Hkv, w.Nkv, w.D))
+    if w.value_scale != 1.0:
+        q *= w.value_scale
+        k *= w.value_scale
+        v *= w.value_scale
+    return rng, q, k, v
+
+
+def make_inputs(w: Workload):
+    """CPU torch tensors (q, k, v) in the workload's storage dtype.
+
+    For fp8 workloads returns (q8, k8, v8, descales) where the codes are
+    ``torch.float8_e4m3fn`` tensors and ``descales`` is a float32 numpy array
+    [dq, dk, dv].
+    """
+    rng, q, k, v = draw_gaussian_qkv(w)
+    if w.dtype in _TORCH_DTYPE:
+        dt = _TORCH_DTYPE[w.dtype]
+        return tuple(torch.from_numpy(x).to(dt) for x in (q, k, v))
+    if w.dtype != "fp8":
+        raise ValueError(f"unknown dtype {w.dtype}")
+    out, desc = [], []
+    for x in (q, k, v):
+        H, D = x.shape[1], x.shape[3]
+        n_out = int(round(w.outlier_frac * H * D))
+        if n_out:
+            cols = rng.choice(H * D, size=n_out, replace=False)
+            hh, dd = np.divmod(cols, D)
+            x[:, hh, :, dd] *= w.outlier_mult
+        code, d = quantize_e4m3(x)
+        out.append(code)
+        desc.append(d)
+    return out[0], out[1], out[2], np.array(desc, dtype=np.float32)
+
+
+def quantize_e4m3(x):
+    """Per-tensor absmax quantisation to e4m3fn: (codes, float32 descale)."""
+    amax = float(np.abs(x).max())
+    descale = np.float32(amax / E4M3FN_MAX) if amax > 0 else np.float32(1.0)
+    y = np.clip(x / np.float64(descale), -E4M3FN_MAX, E4M3FN_MAX)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn), descale
+
+
+def random_problem(B, Hq, Hkv, Nq, Nkv, D, dtype="bf16", seed=0, value_scale=1.0, causal=False):
+    """Inputs for an ad-hoc shape (tests): same recipe as the named workloads."""
+    w = Workload("adhoc", B, Hq, Hkv, Nq, Nkv, D, causal, dtype, value_scale=value_scale, seed=seed)
+    return w, make_inputs(w)

@@ -1,0 +1,34 @@
+"""Plain, slow, fp64 CPU oracle for exact attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in
+this package.  The GPU library never routes through it, and it shares no code
+with the HIP path: no kernels, headers, helpers, tables or pre/post-processing.
+
+Contents
+--------
+exact          -- the plain definition: S = scale*Q K^T materialised per head,
+                  masked, stable softmax, P V and the natural-log LSE.
+online         -- the online-softmax recurrence over key blocks (running max m,
+                  running sum l, rescaled output), used only to pin that the
+                  blockwise algorithm reproduces the plain definition.
+e4m3           -- decoding of OCP FP8 E4M3FN codes to exact float64 values.
+
+Every function cites the passage of the source pages it follows, by page title
+and section.  No function here is "parity unpinned": each one is pinned by a
+test in ``tests/test_oracle_pins.py`` (closed forms, invariants, brute force,
+a library cross-check and a hand-worked example under ``tests/golden/``).
+"""
+from .exact import attention, attention_head, kv_head_of, visible_mask
+from .online import online_attention_head
+from .e4m3 import e4m3fn_decode, E4M3FN_MAX
+
+__all__ = [
+    "attention",
+    "attention_head",
+    "kv_head_of",
+    "visible_mask",
+    "online_attention_head",
+    "e4m3fn_decode",
+    "E4M3FN_MAX",
+]

@@ -1,0 +1,368 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``check_*`` function returns True when the oracle agrees with a fact
+that does not come from the oracle itself: a hand-worked example stored under
+``tests/golden/``, closed forms (identical keys, one-hot logits, V of ones,
+scale 0), invariants (row shifts, permutations, the LSE merge), brute force
+with scalar loops and ``math.fsum`` on tiny shapes, and a library cross-check
+against torch's CPU fp64 scaled-dot-product attention.  The tests assert that
+every check passes; ``test_planted_mistakes_are_caught`` then plants plausible
+mistakes in the oracle (on the CPU) and asserts that some check fails for each.
+"""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.exact as oatt
+from oracle import attention, attention_head, e4m3fn_decode, online_attention_head
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng_arrays(seed, *shapes):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(s) for s in shapes]
+
+
+# ----------------------------------------------------------------------------
+# checks
+# ----------------------------------------------------------------------------
+
+def check_golden():
+    """Hand-worked softmax example (tests/golden/softmax_worked_example.json)."""
+    with open(os.path.join(GOLDEN, "softmax_worked_example.json")) as f:
+        g = json.load(f)
+    q = np.array(g["q"])
+    k = np.log(np.array(g["k_is_log_of"]))
+    v = np.array(g["v"])
+    ok = True
+    for causal, key in ((False, "noncausal"), (True, "causal")):
+        O, lse = attention_head(q, k, v, g["scale"], causal=causal)
+        ok &= np.allclose(O, np.array(g[key]["O"]), rtol=0, atol=1e-12)
+        ok &= np.allclose(lse, np.log(np.array(g[key]["LSE_is_log_of"])), rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def _brute(q, k, v, scale, causal):
+    """Scalar loops with math.fsum over one (b, head); independent of numpy."""
+    Nq, D = q.shape
+    Nkv = k.shape[0]
+    O = [[0.0] * v.shape[1] for _ in range(Nq)]
+    L = [0.0] * Nq
+    for i in range(Nq):
+        vis = [j for j in range(Nkv) if (not causal) or j <= i + Nkv - Nq]
+        if not vis:
+            L[i] = -math.inf
+            continue
+        s = {j: scale * math.fsum(float(q[i, d]) * float(k[j, d]) for d in range(D)) for j in vis}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in vis}
+        tot = math.fsum(w.values())
+        for c in range(v.shape[1]):
+            O[i][c] = math.fsum(w[j] * float(v[j, c]) for j in vis) / tot
+        L[i] = mx + math.log(tot)
+    return np.array(O), np.array(L)
+
+
+def check_brute_force():
+    ok = True
+    cases = [(1, 4, 2, 5, 5, 3, True), (2, 4, 2, 3, 7, 4, True), (1, 4, 1, 8, 6, 8, True),
+             (1, 2, 2, 6, 4, 5, False), (1, 4, 2, 7, 3, 2, True)]
+    for seed, (B, Hq, Hkv, Nq, Nkv, D, causal) in enumerate(cases):
+        q, k, v = rng_arrays(seed, (B, Hq, Nq, D), (B, Hkv, Nkv, D), (B, Hkv, Nkv, D))
+        scale = 0.37 + 0.1 * seed
+        O, L = attention(q, k, v, scale, causal)
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                Ob, Lb = _brute(q[b, h], k[b, h // G], v[b, h // G], scale, causal)
+                ok &= np.allclose(O[b, h], Ob, rtol=0, atol=1e-12)
+                fin = np.isfinite(Lb)
+                ok &= bool(np.array_equal(fin, np.isfinite(L[b, h])))
+                ok &= np.allclose(L[b, h][fin], Lb[fin], rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_library_sdpa():
+    """torch CPU fp64 SDPA (and its flash-for-cpu op for the LSE), Nq == Nkv."""
+    ok = True
+    for seed, (B, Hq, Hkv, N, D, causal) in enumerate([(2, 4, 2, 33, 16, True), (1, 6, 3, 50, 8, False),
+                                                       (1, 2, 2, 17, 32, True)]):
+        q, k, v = rng_arrays(100 + seed, (B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D))
+        scale = 1.0 / math.sqrt(D)
+        O, L = attention(q, k, v, scale, causal)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        G = Hq // Hkv
+        tk = tk.repeat_interleave(G, dim=1)
+        tv = tv.repeat_interleave(G, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+        _, lse = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+            tq, tk, tv, 0.0, causal, attn_mask=None, scale=scale)
+        ok &= np.allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+        ok &= np.allclose(L, lse.numpy(), rtol=0, atol=1e-10)
+    return bool(ok)
+
+
+def check_rows_sum_to_one():
+    q, k = rng_arrays(7, (1, 2, 40, 16), (1, 2, 40, 16))
+    v = np.ones((1, 2, 40, 16))
+    ok = True
+    for causal in (False, True):
+        O, _ = attention(q * 3, k, v, 0.7, causal)
+        ok &= np.allclose(O, 1.0, rtol=0, atol=1e-13)
+    return bool(ok)
+
+
+def check_identical_keys():
+    """All keys equal -> O_i is the mean of visible V rows, LSE = s + ln(n_vis)."""
+    Nq, Nkv, D = 9, 12, 5
+    q, krow, v = rng_arrays(8, (Nq, D), (1, D), (Nkv, D))
+    k = np.repeat(krow, Nkv, axis=0)
+    ok = True
+    for causal in (False, True):
+        O, L = attention_head(q, k, v, 0.9, causal)
+        for i in range(Nq):
+            n = Nkv if not causal else min(Nkv, i + Nkv - Nq + 1)
+            ok &= np.allclose(O[i], v[:n].mean(axis=0), rtol=0, atol=1e-12)
+            s = 0.9 * float(q[i] @ krow[0])
+            ok &= abs(L[i] - (s + math.log(n))) < 1e-12
+    # scale 0: mean of V, LSE = ln(n)
+    q, k, v = rng_arrays(9, (6, 4), (6, 4), (6, 4))
+    O, L = attention_head(q, k, v, 0.0, False)
+    ok &= np.allclose(O, v.mean(axis=0), rtol=0, atol=1e-12)
+    ok &= np.allclose(L, math.log(6), rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_one_hot():
+    """Dominant logit at key t_i selects row t_i of V (error below e^-40)."""
+    Nq, Nkv, D = 6, 10, 8
+    rng = np.random.default_rng(11)
+    t = rng.integers(0, Nkv, size=Nq)
+    alpha, scale = 80.0, 0.5
+    q = np.zeros((Nq, D))
+    q[:, 0] = alpha
+    k = np.zeros((Nkv, D))
+    k[:, 1:] = rng.standard_normal((Nkv, D - 1))
+    v = rng.standard_normal((Nkv, D))
+    O = np.zeros((Nq, D))
+    ok = True
+    for i in range(Nq):
+        kk = k.copy()
+        kk[t[i], 0] = 1.0
+        Oi, Li = attention_head(q[i:i + 1], kk, v, scale, False)
+        ok &= np.allclose(Oi[0], v[t[i]], rtol=0, atol=1e-15 + 20 * math.exp(-40))
+        ok &= abs(Li[0] - alpha * scale) < 1e-12
+    return bool(ok)
+
+
+def check_row_shift():
+    """Adding c_i to every score of row i leaves O fixed and shifts LSE by c_i."""
+    Nq, Nkv, D = 7, 11, 6
+    q, k, v = rng_arrays(12, (Nq, D), (Nkv, D), (Nkv, D))
+    c = np.random.default_rng(13).standard_normal(Nq) * 5
+    scale = 0.4
+    k2 = np.concatenate([k, np.ones((Nkv, 1))], axis=1)
+    q0 = np.concatenate([q, np.zeros((Nq, 1))], axis=1)
+    q2 = np.concatenate([q, (c / scale)[:, None]], axis=1)
+    ok = True
+    for causal in (False, True):
+        O0, L0 = attention_head(q0, k2, v, scale, causal)
+        O1, L1 = attention_head(q2, k2, v, scale, causal)
+        ok &= np.allclose(O0, O1, rtol=0, atol=1e-12)
+        ok &= np.allclose(L1 - L0, c, rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_causal_prefix():
+    """Causal row i equals non-causal attention over keys 0..i (Nq == Nkv)."""
+    N, D = 10, 4
+    q, k, v = rng_arrays(14, (N, D), (N, D), (N, D))
+    O, L = attention_head(q, k, v, 0.8, True)
+    ok = np.allclose(O[0], v[0], rtol=0, atol=1e-15)
+    ok &= abs(L[0] - 0.8 * float(q[0] @ k[0])) < 1e-14
+    for i in range(N):
+        Oi, Li = attention_head(q[i:i + 1], k[:i + 1], v[:i + 1], 0.8, False)
+        ok &= np.allclose(O[i], Oi[0], rtol=0, atol=1e-13)
+        ok &= abs(L[i] - Li[0]) < 1e-13
+    return bool(ok)
+
+
+def check_gqa_repeat():
+    """GQA equals MHA with K/V repeated G times along heads (contiguous groups)."""
+    B, Hq, Hkv, N, D = 2, 6, 2, 9, 4
+    q, k, v = rng_arrays(15, (B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D))
+    O, L = attention(q, k, v, 0.6, True)
+    G = Hq // Hkv
+    O2, L2 = attention(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.6, True)
+    return bool(np.allclose(O, O2, rtol=0, atol=0) and np.allclose(L, L2, rtol=0, atol=0))
+
+
+def check_merge():
+    """Split the keys in two: logaddexp of the LSEs and the LSE-weighted O."""
+    Nq, Nkv, D = 8, 20, 5
+    q, k, v = rng_arrays(16, (Nq, D), (Nkv, D), (Nkv, D))
+    O, L = attention_head(q, k, v, 0.5, False)
+    O1, L1 = attention_head(q, k[:7], v[:7], 0.5, False)
+    O2, L2 = attention_head(q, k[7:], v[7:], 0.5, False)
+    Lm = np.logaddexp(L1, L2)
+    Om = np.exp(L1 - Lm)[:, None] * O1 + np.exp(L2 - Lm)[:, None] * O2
+    return bool(np.allclose(L, Lm, rtol=0, atol=1e-12) and np.allclose(O, Om, rtol=0, atol=1e-12))
+
+
+def check_permutations():
+    Nq, Nkv, D = 7, 13, 3
+    q, k, v = rng_arrays(17, (Nq, D), (Nkv, D), (Nkv, D))
+    rng = np.random.default_rng(18)
+    pk, pq = rng.permutation(Nkv), rng.permutation(Nq)
+    O, L = attention_head(q, k, v, 0.5, False)
+    O1, L1 = attention_head(q, k[pk], v[pk], 0.5, False)
+    O2, L2 = attention_head(q[pq], k, v, 0.5, False)
+    ok = np.allclose(O, O1, rtol=0, atol=1e-12) and np.allclose(L, L1, rtol=0, atol=1e-12)
+    ok &= np.allclose(O[pq], O2, rtol=0, atol=1e-12) and np.allclose(L[pq], L2, rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_no_visible_rows():
+    """Causal with Nq > Nkv: the first Nq - Nkv rows see nothing -> O = 0, LSE = -inf."""
+    q, k, v = rng_arrays(19, (9, 4), (5, 4), (5, 4))
+    O, L = attention_head(q, k, v, 0.5, True)
+    ok = np.all(O[:4] == 0) and np.all(np.isneginf(L[:4])) and np.all(np.isfinite(L[4:]))
+    ok &= np.allclose(O[4], v[0], rtol=0, atol=1e-15)
+    return bool(ok)
+
+
+def check_rows_subset():
+    """Computing only some rows gives exactly those rows of the full result."""
+    q, k, v = rng_arrays(20, (30, 8), (40, 8), (40, 8))
+    rows = np.array([0, 3, 17, 29])
+    ok = True
+    for causal in (False, True):
+        O, L = attention_head(q, k, v, 0.3, causal)
+        Os, Ls = attention_head(q, k, v, 0.3, causal, rows=rows)
+        ok &= np.array_equal(O[rows], Os) and np.array_equal(L[rows], Ls)
+    return bool(ok)
+
+
+ALL_CHECKS = [check_golden, check_brute_force, check_library_sdpa, check_rows_sum_to_one,
+              check_identical_keys, check_one_hot, check_row_shift, check_causal_prefix,
+              check_gqa_repeat, check_merge, check_permutations, check_no_visible_rows,
+              check_rows_subset]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    assert check()
+
+
+# ----------------------------------------------------------------------------
+# the online recurrence (what the kernel runs) reproduces the plain definition
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tau", [0.0, 0.125, 3.0, 8.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_recurrence_matches_definition(tau, causal):
+    for seed, (Nq, Nkv, D) in enumerate([(37, 37, 16), (20, 53, 8), (53, 20, 8), (64, 64, 32)]):
+        q, k, v = rng_arrays(200 + seed, (Nq, D), (Nkv, D), (Nkv, D))
+        q *= 2.5  # widen the score range so the running max moves often
+        O, L = attention_head(q, k, v, 0.35, causal)
+        blocks = tuple(np.random.default_rng(seed).integers(1, 17, size=5))
+        O2, L2 = online_attention_head(q, k, v, 0.35, causal, block_sizes=blocks, tau=tau)
+        assert np.allclose(O, O2, rtol=0, atol=1e-12)
+        fin = np.isfinite(L)
+        assert np.array_equal(fin, np.isfinite(L2))
+        assert np.allclose(L[fin], L2[fin], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# e4m3 decoding
+# ----------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_library_and_spec():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3fn_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ours[~nan], lib[~nan])
+    # constants fixed by the OCP definition
+    assert ours[0x7E] == oracle.E4M3FN_MAX == 448.0
+    assert ours[0x08] == 2.0 ** -6           # smallest normal
+    assert ours[0x01] == 2.0 ** -9           # smallest subnormal
+    assert ours[0x38] == 1.0 and ours[0xB8] == -1.0
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+    pos = ours[:0x7F]
+    assert np.all(np.diff(pos) > 0)          # codes 0..126 increase strictly
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must make at least one check fail
+# ----------------------------------------------------------------------------
+
+def _mut_gqa(hq, Hq, Hkv):
+    return hq % Hkv
+
+
+def _mut_topleft(Nq, Nkv, causal, rows=None):
+    if rows is None:
+        rows = np.arange(Nq)
+    rows = np.asarray(rows)
+    j = np.arange(Nkv)[None, :]
+    return np.ones((rows.size, Nkv), bool) if not causal else j <= rows[:, None]
+
+
+def _mut_strict(Nq, Nkv, causal, rows=None):
+    if rows is None:
+        rows = np.arange(Nq)
+    rows = np.asarray(rows)
+    j = np.arange(Nkv)[None, :]
+    return np.ones((rows.size, Nkv), bool) if not causal else j < rows[:, None] + (Nkv - Nq)
+
+
+_real_head = oatt.attention_head
+
+
+def _mut_no_scale(q, k, v, scale, causal=False, rows=None):
+    return _real_head(q, k, v, 1.0, causal, rows)
+
+
+def _mut_lse_log2(q, k, v, scale, causal=False, rows=None):
+    O, L = _real_head(q, k, v, scale, causal, rows)
+    return O, L / math.log(2.0)
+
+
+def _mut_v_reversed(q, k, v, scale, causal=False, rows=None):
+    return _real_head(q, k, np.asarray(v)[::-1], scale, causal, rows)
+
+
+def _mut_sqrt_scale(q, k, v, scale, causal=False, rows=None):
+    return _real_head(q, k, v, math.sqrt(abs(scale)), causal, rows)
+
+
+MUTATIONS = {
+    "gqa_modulo": ("kv_head_of", _mut_gqa),
+    "causal_top_left": ("visible_mask", _mut_topleft),
+    "causal_strict": ("visible_mask", _mut_strict),
+    "scale_dropped": ("attention_head", _mut_no_scale),
+    "lse_base2": ("attention_head", _mut_lse_log2),
+    "v_rows_misindexed": ("attention_head", _mut_v_reversed),
+    "scale_sqrt": ("attention_head", _mut_sqrt_scale),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oatt, attr, fn)
+    # the checks call through the module so that the mutation is seen
+    monkeypatch.setattr(oracle, "attention_head", oatt.attention_head, raising=False)
+    me = sys.modules[__name__]
+    monkeypatch.setattr(me, "attention_head", oatt.attention_head)
+    failed = [c.__name__ for c in ALL_CHECKS if not c()]
+    assert failed, f"no check caught the planted mistake {name}"
