@@ -1,0 +1,178 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one forward pass (one ``attn_fwd`` launch) over the whole batch of
+the workload, inputs resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Throughput is matmul TFLOP/s: 4 * B * Hq * D * (visible query/key pairs) per
+step (the QK^T and PV products; softmax work is not counted).  The roofline
+object prices the same flops against the dense MFMA peak of the compute dtype,
+using the kernel's own average duration from HIP events recorded on the
+launch stream.  The cpu_baseline object times the fp64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from exact_io_aware_attn_amd import attn as A
+from exact_io_aware_attn_amd.inputs import WORKLOADS, make_inputs
+
+METRIC = "attention fwd TFLOPS on 1 MI355X and % of dense bf16/fp8 MFMA peak"
+# MI355X dense MFMA peaks (TFLOP/s): bf16 2.5 PF, fp8 5.0 PF, fp32 157.3 TF.
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "prefill_causal_bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+def gpu_inputs(w, dev):
+    inp = make_inputs(w)
+    if w.dtype == "fp8":
+        q8, k8, v8, desc = inp
+        ds = [torch.tensor([float(x)], dtype=torch.float32, device=dev) for x in desc]
+        return (q8.to(dev), k8.to(dev), v8.to(dev), *ds), inp
+    return tuple(t.to(dev) for t in inp), inp
+
+
+def make_step(w, dev_inp, out, lse):
+    if w.dtype == "fp8":
+        q, k, v, dq, dk, dv = dev_inp
+        return lambda: A.fwd_fp8(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse)
+    q, k, v = dev_inp
+    return lambda: A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)
+
+
+def cpu_baseline(w, host_inp, n_heads):
+    """Time the fp64 oracle on n_heads (batch, head) pairs of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    G = w.Hq // w.Hkv
+    rng = np.random.default_rng(1)
+    heads = [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads)]
+    if w.dtype == "fp8":
+        q8, k8, v8, desc = host_inp
+
+        def head(t, d, b, h):
+            return oracle.e4m3fn_decode(t[b, h].view(torch.uint8).numpy()) * np.float64(d)
+        get_q = lambda b, h: head(q8, desc[0], b, h)
+        get_k = lambda b, h: head(k8, desc[1], b, h)
+        get_v = lambda b, h: head(v8, desc[2], b, h)
+    else:
+        q, k, v = host_inp
+        get_q = lambda b, h: q[b, h].to(torch.float64).numpy()
+        get_k = lambda b, h: k[b, h].to(torch.float64).numpy()
+        get_v = lambda b, h: v[b, h].to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    for b, hq in heads:
+        oracle.attention_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * w.visible_pairs * len(heads)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(heads)} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 numpy, "
+                  f"S materialised per head; {dt:.1f} s wall, scaled by the same flop formula",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    A.lib()  # fail loudly if the HIP library is missing
+    dev_inp, host_inp = gpu_inputs(w, dev)
+    out_dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=out_dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    step = make_step(w, dev_inp, out, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in ev]
+    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / avg_kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
+            "causal": w.causal, "scale": "1/sqrt(D)", "inputs": "i.i.d. N(0,1), seed 0",
+            "flops_per_step": flops,
+            "pct_of_dense_peak": round(100.0 * value / peak, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_heads or (6 if w.Nq * w.Nkv <= 4096 * 4096 else 2)
+        res["cpu_baseline"] = cpu_baseline(w, host_inp, n)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

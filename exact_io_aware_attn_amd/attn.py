@@ -1,0 +1,149 @@
+"""ctypes binding of ``libattn.so`` (the C ABI declared in ``include/attn.h``).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI.  Torch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails,
+``AttnError`` is raised.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+
+# every symbol include/attn.h declares
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    """A failed call into the attention library (or the library is missing)."""
+
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load ``libattn.so`` once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise AttnError(-1, f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_attn_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, vp]
+    L.attn_fwd.restype = ci
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
+    L.attn_fwd_fp8.restype = ci
+    L.attn_status_string.argtypes = [ci]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ci
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != ATTN_OK:
+        L = lib()
+        raise AttnError(status, f"{L.attn_status_string(status).decode()}: {L.attn_last_error().decode()}")
+
+
+def raw_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, stream=0):
+    """Call ``attn_fwd`` with raw integer pointers; returns the status code."""
+    return lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), int(dtype), stream)
+
+
+def raw_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dq, dk, dv, stream=0):
+    """Call ``attn_fwd_fp8`` with raw integer pointers; returns the status code."""
+    return lib().attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dq, dk, dv,
+                              stream)
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, H, N, D)")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    return B, Hq, Hkv, Nq, Nkv, D
+
+
+def _stream_ptr(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True, stream=None):
+    """Exact attention forward on the GPU.
+
+    q: (B, Hq, Nq, D), k/v: (B, Hkv, Nkv, D); dtype float32 or bfloat16.
+    Returns (o, lse): o has q's dtype, lse is float32 (B, Hq, Nq) (None if
+    ``return_lse`` is False).  ``scale`` defaults to 1/sqrt(D).
+    """
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    if q.dtype == torch.float32:
+        dt = ATTN_F32
+    elif q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype} (use fwd_fp8 for e4m3)")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                   lse.data_ptr() if lse is not None else None,
+                   B, Hq, Hkv, Nq, Nkv, D, causal, scale, dt, _stream_ptr(stream)))
+    return out, lse
+
+
+def fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=False, scale=None, out=None,
+            lse=None, return_lse=True, stream=None):
+    """Exact attention forward on per-tensor-scaled e4m3fn inputs (bf16 out).
+
+    q/k/v: ``torch.float8_e4m3fn`` device tensors; descales: one-element
+    float32 device tensors (or None for 1.0).  ``scale`` defaults to 1/sqrt(D).
+    """
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    for t in (q, k, v):
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError("fwd_fp8 takes torch.float8_e4m3fn tensors")
+    ptrs = []
+    for d in (descale_q, descale_k, descale_v):
+        if d is None:
+            ptrs.append(None)
+            continue
+        if d.dtype != torch.float32 or not d.is_cuda or d.numel() < 1:
+            raise ValueError("descales must be float32 device tensors with one element")
+        ptrs.append(d.data_ptr())
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(raw_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if lse is not None else None,
+                       B, Hq, Hkv, Nq, Nkv, D, causal, scale, *ptrs, _stream_ptr(stream)))
+    return out, lse

@@ -1,0 +1,137 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact attention forward library.
+ *
+ * The library computes, without ever writing the Nq x Nkv score matrix to
+ * memory, the exact attention forward pass
+ *
+ *     O = softmax(scale * Q K^T + mask) V,    LSE = log-sum-exp of each row,
+ *
+ * by tiling Q into row blocks and streaming K/V tiles through on-chip memory
+ * with the online softmax (running row max m, running row sum l, rescaled
+ * output accumulator).  Sources: FlashAttention summary page (method
+ * paragraph: tiles in SRAM, running (m, l) and output kept on chip, exact);
+ * FlashAttention v1/v2/v3/v4 blog post, section "El truco que hizo posible
+ * todo: online softmax" (the recurrence); FFPA README, section "Split-D and
+ * TiledMMA" (head dims 320..1024 by chunking D).
+ *
+ * Semantics shared by every entry point
+ * -------------------------------------
+ *  Layout (FFPA README, "Quick Start": layout follows SDPA, (B, H, N, D)):
+ *    q   : (B, Hq,  Nq,  D) contiguous, row-major
+ *    k, v: (B, Hkv, Nkv, D) contiguous, row-major
+ *    o   : (B, Hq,  Nq,  D) contiguous, row-major
+ *    lse : (B, Hq,  Nq)     contiguous float32, natural log; may be NULL
+ *  GQA/MQA (FFPA README feature table; ZYFA article, "Who should actually run
+ *    it"): Hq must be a multiple of Hkv; query head hq reads KV head
+ *    hq / (Hq / Hkv) (contiguous groups).  Cross attention: Nq != Nkv.
+ *  Causal (causal != 0): key j is visible to query i iff j <= i + (Nkv - Nq)
+ *    (bottom-right alignment; equal to top-left when Nq == Nkv).  A row that
+ *    sees no key gets O = 0 and LSE = -inf.
+ *  scale multiplies Q K^T before the mask and softmax; any finite value.
+ *  LSE_i = ln(sum over visible j of exp(s_ij)) in float32.
+ *  Every element of o and lse is written; no other memory is written.
+ *  Results are bitwise identical from launch to launch (no atomics, fixed
+ *  reduction order) -- ZYFA article, "The details that make it
+ *  production-grade" (determinism; LSE lets key-range results merge).
+ *
+ *  Supported sizes: B, Hq, Hkv, Nq, Nkv >= 1; D a multiple of 32 in
+ *    [32, 256] for every dtype, and additionally D in [288, 1024] (multiple of
+ *    32) for ATTN_BF16 via the split-D kernels; each (batch, head) slab of q,
+ *    k, v and o must be smaller than 2^31 bytes; B*Hq*ceil(Nq/64) < 2^31.
+ *
+ * Ownership, synchronisation and errors
+ * -------------------------------------
+ *  All tensor pointers are DEVICE pointers owned by the caller; they must stay
+ *  valid until the enqueued work on `stream` completes.  Pointers must be
+ *  16-byte aligned.  The calls are asynchronous: they validate, enqueue one
+ *  kernel on `stream` (NULL = the default stream) and return without
+ *  synchronising the host.  The library allocates no memory and keeps no
+ *  per-shape state, so calls may be captured into a HIP graph.
+ *  Return value: ATTN_OK, or an attn_status code.  On a validation failure
+ *  nothing is enqueued.  ATTN_ERR_HIP reports a launch failure returned by
+ *  the HIP runtime (for example: no device).  Faults inside the kernel
+ *  surface at the caller's next synchronisation, as usual in HIP.  A
+ *  human-readable description of the last failure on the calling thread is
+ *  returned by attn_last_error().  No C++ exception crosses this boundary.
+ */
+#ifndef EXACT_IO_AWARE_ATTN_AMD_ATTN_H
+#define EXACT_IO_AWARE_ATTN_AMD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t is an opaque pointer; the ABI takes it as void* so that this
+ * header needs no HIP include. */
+typedef void* attn_stream_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* NULL pointer, size < 1, Hq % Hkv != 0, non-finite
+                               scale, unknown dtype, misaligned pointer,
+                               non-positive or non-finite descale value */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid but outside the supported D / size range */
+  ATTN_ERR_HIP = 3          /* the HIP runtime refused the launch */
+} attn_status;
+
+typedef enum {
+  ATTN_F32 = 0,      /* q, k, v, o float32; products and softmax in float32  */
+  ATTN_BF16 = 1,     /* q, k, v, o bfloat16; float32 accumulation and softmax */
+  ATTN_FP8_E4M3 = 2  /* q, k, v OCP e4m3fn codes; o bfloat16 (see attn_fwd_fp8) */
+} attn_dtype;
+
+/*
+ * attn_fwd -- exact attention forward (see the semantics above).
+ *   q, k, v : device inputs of element type `dtype`
+ *   o       : device output; float32 for ATTN_F32, bfloat16 otherwise
+ *   lse     : device float32 output (B, Hq, Nq), or NULL to skip it
+ *   B, Hq, Hkv, Nq, Nkv, D : sizes (see "Supported sizes")
+ *   causal  : 0 = no mask, nonzero = bottom-right causal mask
+ *   scale   : multiplier of Q K^T (the caller passes 1/sqrt(D) for SDPA's
+ *             default)
+ *   dtype   : attn_dtype; ATTN_FP8_E4M3 here means all descales equal 1
+ *   stream  : hipStream_t to enqueue on (NULL = default stream)
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+             int causal, float scale, int dtype, attn_stream_t stream);
+
+/*
+ * attn_fwd_fp8 -- exact attention forward on per-tensor-scaled e4m3 inputs.
+ * ZYFA article, sections "Getting started with ZYFA" and "Who should actually
+ * run it": FP8 calls take one descale per tensor and the kernel reads the
+ * descales from GPU memory, so a call never waits on the host.
+ *   q, k, v    : OCP e4m3fn codes (1 byte each), layouts as above
+ *   descale_q, descale_k, descale_v : DEVICE pointers to one float32 each
+ *                (the value each code is multiplied by); NULL means 1.0.
+ *                The values must be positive and finite; they are read by the
+ *                kernel, so the host never checks them.
+ *   o          : bfloat16 output; lse as above
+ * Computed: s_ij = scale * dq * dk * (q8_i . k8_j), O = dv * softmax(s) v8.
+ * Q K^T runs on the fp8 matrix cores; P V runs with P rounded to bfloat16
+ * and the e4m3 values of V widened exactly to bfloat16.  Supported D:
+ * multiples of 64 in [64, 256].
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                 int causal, float scale,
+                 const float* descale_q, const float* descale_k, const float* descale_v,
+                 attn_stream_t stream);
+
+/* Static English name of a status code ("ATTN_OK", ...); never NULL. */
+const char* attn_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none).  The
+ * pointer stays valid until the next call of this library on this thread. */
+const char* attn_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_ATTN_AMD_ATTN_H */
