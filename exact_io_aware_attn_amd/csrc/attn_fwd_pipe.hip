@@ -1,0 +1,358 @@
+// attn_fwd_pipe.hip -- bf16 attention forward for gfx950 with direct-to-LDS
+// K/V streaming (head dims 64 and 128, positive scale).
+//
+// Same algorithm as the generic tiled kernel (FlashAttention summary page,
+// method paragraph; blog post "FlashAttention v1/v2/v3/v4", section "El truco
+// que hizo posible todo: online softmax"), laid out for the MI355X pipes:
+//
+//  * Each wave owns 32 query rows; a work-group of 4 waves owns 128 rows and
+//    two work-groups share a CU, so every SIMD runs two waves from two
+//    independent work-groups.  Their barriers are independent, so while one
+//    wave runs its exp/sum/convert work on the vector ALU the other keeps the
+//    matrix pipe busy (the ZYFA article, sections "Why FP8 attention is
+//    softmax-bound on MI355X" and "The three techniques, in plain terms",
+//    explains why this overlap decides the speed on this GPU).
+//  * K and V tiles move HBM/L2 -> LDS with buffer loads that write LDS
+//    directly (no staging registers, no LDS store instructions); the range
+//    check of the buffer resource zero-fills keys past Nkv.  Two buffers per
+//    operand: the loads of tile t+1 are issued at the top of iteration t and
+//    waited for at its end, one barrier per iteration.  The loads are issued
+//    from inline assembly so that the compiler's own wait insertion, which
+//    cannot tell the two buffers apart, does not stall every LDS read on
+//    them; the kernel waits for them explicitly before its barrier.
+//  * LDS layouts are unpadded with XOR swizzles on 16-byte chunks: K rows use
+//    chunk ^ (row & 7), so the 8 lanes of an LDS phase read 8 distinct bank
+//    groups; V rows use chunk ^ 2*(row & 3), matching the 4-row x 32-byte
+//    footprint of each 16-lane group of the transposing LDS read.
+//  * V is never transposed in registers: ds_read_b64_tr_b16 returns, for
+//    each lane, four consecutive keys of one head-dim column, which is
+//    exactly the A operand of O^T += V^T P^T.
+//  * Row sums add the fp32 probabilities before rounding: a sum of the
+//    bf16-rounded values would move the LSE of short (early causal) rows by
+//    up to ~2^-9 relative.
+//  * Lazy rescale (ZYFA article, "The details that make it
+//    production-grade"): the running max moves, and O and l are rescaled,
+//    only when a row's new max exceeds it by more than 8 (base-2 units).
+//    With a stale max the probabilities are at most 2^8, which bf16 and the
+//    fp32 accumulators hold as well as values <= 1; O/l and m + log2(l) are
+//    unchanged, so the result is still exact.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D, int NW, int QB>
+struct PipeCfg {
+  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int NT = NW * 64;            // threads per work-group
+  static constexpr int QW = QB * 32;            // query rows per wave
+  static constexpr int BR = NW * QW;            // query rows per work-group
+  static constexpr int RP = D * 2;              // LDS row pitch (bytes)
+  static constexpr int TILE = BC * RP;          // bytes of one K or V tile
+  static constexpr int DMA_TILE = TILE / 1024;  // wave-wide 16 B/lane loads per tile
+  static constexpr int DMA_WAVE = DMA_TILE / NW;
+  static constexpr int NDB = D / 32;            // 32-row blocks of O^T
+  static constexpr int NQC = D / 16;            // 16-wide d chunks of the QK^T contraction
+  static constexpr int NKB = BC / 32;           // 32-key blocks of S^T per tile
+  static constexpr int LDS = 4 * TILE;          // K0, K1, V0, V1
+  static_assert(D % 64 == 0, "D must be a multiple of 64");
+  static_assert(DMA_TILE % NW == 0, "tile must split evenly over the waves");
+};
+
+// XOR swizzles on the 16-byte chunk index of a row (both stay inside an
+// aligned group of 8 chunks, so any D that is a multiple of 64 works).
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, stride 0, num_records = nbytes, gfx9 raw
+// format) in scalar registers, for the inline-assembly loads below.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// Issue the direct-to-LDS loads of one K (IS_V = false) or V tile.  Each
+// wave fills DMA_WAVE consecutive 1 KiB blocks; lane l writes bytes
+// [16 l, 16 l + 16) of a block (M0 holds the block's LDS address), so the
+// global chunk it fetches is the one the swizzle places there.  Offsets at or
+// past num_records read as zero.
+template <typename C, bool IS_V>
+__device__ __forceinline__ void dma_tile(i32x4 rsrc, const char* dst, int kt, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::DMA_WAVE; ++j) {
+    const int blk = wave * C::DMA_WAVE + j;
+    const int o = blk * 1024 + lane * 16;
+    const int row = o / C::RP;
+    const int pc = (o % C::RP) >> 4;
+    const int gc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
+    const uint32_t voff = (uint32_t)(kt * C::BC + row) * (uint32_t)C::RP + (uint32_t)(gc << 4);
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(dst + blk * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
+  using C = PipeCfg<D, NW, QB>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  char* const kbuf0 = lds;
+  char* const kbuf1 = lds + C::TILE;
+  char* const vbuf0 = lds + 2 * C::TILE;
+  char* const vbuf1 = lds + 3 * C::TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  // ---- work decomposition --------------------------------------------------
+  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int qt_raw = wg % p.n_qtiles;
+  const int bh = wg / p.n_qtiles;
+  const int hq = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int qt = p.causal ? (p.n_qtiles - 1 - qt_raw) : qt_raw;
+  const int hk = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int q0w = q0 + wave * C::QW;
+
+  const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab, (uint32_t)((int64_t)p.Nq * D * 2));
+  const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, kv_bytes);
+  const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, kv_bytes);
+
+  const float c = p.scale * kLog2e;  // > 0 (the launcher routes other scales elsewhere)
+
+  // ---- key range ------------------------------------------------------------------
+  int kv_end = p.Nkv;
+  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
+
+  // ---- prologue loads: K0, V0 (LDS), Q (registers) -------------------------------
+  if (n_kt > 0) {
+    dma_tile<C, false>(rk, kbuf0, 0, wave, lane);
+    dma_tile<C, true>(rv, vbuf0, 0, wave, lane);
+  }
+  u32x4 qf[QB][C::NQC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint32_t row_off = (uint32_t)(q0w + qb * 32 + l32) * (uint32_t)(D * 2);
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) qf[qb][cc] = buf_load16(rq, row_off + (uint32_t)(cc * 32 + h * 16));
+  }
+
+  f32x16 acc[QB][C::NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[qb][db] = f32x16{};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+  }
+
+  // per-lane LDS byte offsets that do not change across tiles
+  // K fragment (A operand of S^T = K Q^T): row l32 (+32 kb), chunk 2cc + h
+  uint32_t koff[C::NQC];
+#pragma unroll
+  for (int cc = 0; cc < C::NQC; ++cc) koff[cc] = (uint32_t)(l32 * C::RP + (((2 * cc + h) ^ k_swz(l32)) << 4));
+  // V fragment (A operand of O^T += V^T P^T) via the transposing read: lane r
+  // of each 16-lane group addresses row kbase + r/4, columns dbase + 4(r%4)..+3
+  const int g16 = lane >> 4, r16 = lane & 15;
+  uint32_t voff[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+    const int row = 4 * h + (r16 >> 2);  // + 16 s16 (+ 8): multiples of 4 keep row & 3
+    voff[db] = (uint32_t)(row * C::RP + ((chunk ^ v_swz(row)) << 4) + ((r16 & 1) << 3));
+  }
+  // last visible key of this lane's query row in each block
+  int klim[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = q0w + qb * 32 + l32;
+    klim[qb] = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
+  }
+
+  if (n_kt > 0) {
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const bool odd = kt & 1;
+    const char* const kb_cur = odd ? kbuf1 : kbuf0;
+    const char* const vb_cur = odd ? vbuf1 : vbuf0;
+    if (kt + 1 < n_kt) {
+      dma_tile<C, false>(rk, odd ? kbuf0 : kbuf1, kt + 1, wave, lane);
+      dma_tile<C, true>(rv, odd ? vbuf0 : vbuf1, kt + 1, wave, lane);
+    }
+
+    // ---- S^T = K Q^T ------------------------------------------------------------
+    f32x16 s[QB][C::NKB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int cc = 0; cc < C::NQC; ++cc) {
+        const u32x4 kf = lds_load16(kb_cur, koff[cc] + (uint32_t)(kb * 32 * C::RP));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(kf, qf[qb][cc], s[qb][kb]);
+      }
+    }
+
+    // ---- mask (tiles crossing the diagonal or the key tail only) ------------------
+    const int key0 = kt * C::BC;
+    if ((key0 + C::BC > p.Nkv) || (p.causal && key0 + C::BC - 1 > q0w + p.kv_off)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            s[qb][kb][r] = key <= klim[qb] ? s[qb][kb][r] : -INFINITY;
+          }
+    }
+
+    // ---- online softmax with lazy rescale -----------------------------------------
+    u32x4 pf[QB][2 * C::NKB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+      const float mrow = fmaxf(mx, xor32(mx)) * c;  // scaled (base-2) units
+      if (__builtin_amdgcn_ballot_w64(mrow > m_run[qb] + kTau) != 0) {
+        // rows that have seen no visible key yet keep m = -inf; exp2 of
+        // (-inf) - 0 is 0 there, never (-inf) - (-inf)
+        const float m_new = fmaxf(m_run[qb], mrow);
+        const float alpha = exp2_fast(m_run[qb] - (m_new == -INFINITY ? 0.0f : m_new));
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) acc[qb][db] *= alpha;
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float mneg = m_run[qb] == -INFINITY ? 0.0f : -m_run[qb];
+      float ls = l_run[qb];
+#pragma unroll
+      for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+        const int kb = s16 >> 1, r0 = (s16 & 1) * 8;
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(s[qb][kb][r0 + i], c, mneg));
+        pf[qb][s16].x = pack_bf16x2(e[0], e[1]);
+        pf[qb][s16].y = pack_bf16x2(e[2], e[3]);
+        pf[qb][s16].z = pack_bf16x2(e[4], e[5]);
+        pf[qb][s16].w = pack_bf16x2(e[6], e[7]);
+        ls += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+      l_run[qb] = ls;
+    }
+
+    // ---- O^T += V^T P^T ---------------------------------------------------------------
+#pragma unroll
+    for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const uint32_t a0 = voff[db] + (uint32_t)(s16 * 16 * C::RP);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0 + 8 * C::RP));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 vf = {l2.x, l2.y, h2.x, h2.y};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(vf, pf[qb][s16], acc[qb][db]);
+      }
+    }
+
+    // ---- the next tiles are resident and every wave is done with this one --------
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  // ---- epilogue ---------------------------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + xor32(l_run[qb]);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int qrow = q0w + qb * 32 + l32;
+    if (qrow < p.Nq) {
+      const int64_t orow = q_slab + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * h;
+          u32x2 pk;
+          pk.x = pack_bf16x2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv);
+          pk.y = pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d) = pk;
+        }
+      }
+      if (p.lse != nullptr && h == 0)
+        p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
+            l_tot > 0.0f ? (m_run[qb] + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, int NW, int QB>
+hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
+  using C = PipeCfg<D, NW, QB>;
+  FwdParams p = p0;
+  p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
+  const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
+  if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  p.total_wg = (int)total;
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, QB>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+LaunchFn pipe_launcher(int elt, int D) {
+  if (elt != ELT_BF16) return nullptr;
+  if (D == 128) return &launch_pipe<128, 4, 1>;
+  if (D == 64) return &launch_pipe<64, 4, 1>;
+  return nullptr;
+}
+
+}  // namespace attn

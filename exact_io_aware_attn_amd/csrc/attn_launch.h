@@ -34,6 +34,10 @@ typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 // (attn::Elt) and head dim D, or nullptr if that pair is not instantiated.
 LaunchFn tiled_launcher(int elt, int D);
 
+// Launcher for the software-pipelined bf16 kernel (D in {64, 128}, scale > 0),
+// or nullptr.
+LaunchFn pipe_launcher(int elt, int D);
+
 // Launcher for the split-D kernels (bf16, 256 < D <= 1024), or nullptr.
 LaunchFn splitd_launcher(int elt, int D);
 
