@@ -39,7 +39,22 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0 = auto)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of attention, run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """Plain device-to-device copy of a known size: the bytes the HBM traffic
+    counters should report per launch are exactly 2 x mib MiB (read + write)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                                           "launches": steps}}), flush=True)
 
 
 def gpu_inputs(w, dev):
@@ -107,6 +122,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, args.steps)
+        return
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     A.lib()  # fail loudly if the HIP library is missing
