@@ -1,10 +1,351 @@
-// attn_fwd_splitd.hip -- placeholder translation unit for the split-D kernels
-// (bf16, 256 < D <= 1024).
+// attn_fwd_splitd.hip -- exact attention forward for large head dims
+// (bf16, D a multiple of 64 in [320, 1024]) on gfx950.
+//
+// FFPA README, section "Split-D and TiledMMA": two things grow with D -- the
+// on-chip footprint of the Q/K/V tiles and the registers of the output
+// accumulator.  FFPA breaks the first by chunking D and the second by
+// splitting the P V product's N = D dimension across warps ("M4N2").  The
+// same two ideas, recast for wave64 MFMA and the MI355X register file:
+//
+//  * A work-group has 4 waves = 2 query halves (32 rows each) x 2 head-dim
+//    halves (D/2 columns each).  Wave (qh, dh) keeps Q[32 rows, D/2 cols] in
+//    registers and accumulates O^T[D/2 rows, 32 queries] -- D/8 + D/4
+//    registers per lane, so D = 1024 fits (128 VGPRs of Q, 256 accumulator
+//    registers) where a wave owning all of D would need twice that.  The two
+//    halves are interleaved: for S, wave dh owns the 16-column chunks
+//    2cc + dh; for O, the 32-column blocks 2db + dh.  With the XOR swizzle
+//    acting on the low three bits of the 16-byte chunk index, every fragment
+//    address is then one per-lane base plus a compile-time offset.
+//  * S^T = K Q^T is contracted over D in two halves: each wave of a
+//    (qh, 0)/(qh, 1) pair computes the partial sum over its own D/2 columns,
+//    the pair swaps partials through LDS (4 KiB per wave per tile), and both
+//    add them (fp32 addition is commutative, so both hold bit-identical S).
+//    Both then run the same online softmax (running max m, running sum l;
+//    FA blog "El truco que hizo posible todo: online softmax") and each
+//    multiplies P by its own D/2 columns of V.
+//  * K and V tiles of 32 keys stream into LDS with direct-to-LDS buffer
+//    loads (zero past Nkv) using the same XOR swizzles as the D <= 128
+//    kernel.  At D = 1024 one K tile and one V tile already take 128 KiB of
+//    the 160 KiB LDS, so each is single-buffered and the two loads are
+//    staggered: K(t+1) streams in while the softmax and P V of tile t run, and
+//    V(t+1) streams in while the scores of tile t+1 are computed.  Two
+//    barriers per tile.
+//  * Causal masking, tails, lazy rescale (tau = 8, exact), XCD-contiguous
+//    work-group ranges and heaviest-first causal order as in the other
+//    kernels.
 #include "attn_common.h"
 #include "attn_launch.h"
 
 namespace attn {
 
-LaunchFn splitd_launcher(int, int) { return nullptr; }
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct SplitCfg {
+  static constexpr int NW = 4;                     // (query half) x (head-dim half)
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = 64;                    // query rows per work-group
+  static constexpr int BC = 32;                    // keys per tile
+  static constexpr int DH = D / 2;                 // head-dim columns per wave
+  static constexpr int RP = D * 2;                 // LDS row pitch (bytes)
+  static constexpr int TILE = BC * RP;             // one K or V tile
+  static constexpr int DMA_WAVE = TILE / 1024 / NW;
+  static constexpr int NQC = DH / 16;              // QK^T k-steps per wave (16-col chunks 2cc + dh)
+  static constexpr int NDB = DH / 32;              // 32-row blocks of O^T per wave (blocks 2db + dh)
+  static constexpr int XCH = NW * 64 * 16 * 4;     // partial-S exchange area
+  static constexpr int LDS = 2 * TILE + XCH;
+  static_assert(D % 64 == 0, "D must be a multiple of 64");
+  static_assert((TILE / 1024) % NW == 0, "tile must split evenly over the waves");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// Direct-to-LDS loads of one tile (see the D <= 128 kernel for the layout):
+// wave `wave` fills DMA_WAVE consecutive 1 KiB blocks, lane l writes bytes
+// [16 l, 16 l + 16) of each block.  Loads are issued from inline assembly so
+// the compiler does not stall LDS reads of the other buffer on them.
+template <typename C, bool IS_V>
+__device__ __forceinline__ void dma_tile(i32x4 rsrc, const char* dst, int kt, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::DMA_WAVE; ++j) {
+    const int blk = wave * C::DMA_WAVE + j;
+    const int o = blk * 1024 + lane * 16;
+    const int row = o / C::RP;
+    const int pc = (o % C::RP) >> 4;
+    const int gc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
+    const uint32_t voff = (uint32_t)(kt * C::BC + row) * (uint32_t)C::RP + (uint32_t)(gc << 4);
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(dst + blk * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// acc *= alpha with every element kept in an accumulation register (AGPR).
+// Written as C++, the multiply would make the register allocator hold the
+// loop-carried accumulators in VGPRs and copy all of them to and from AGPRs
+// on every tile (D/4 registers each way); the "a" constraint pins them.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = acc[r], t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(v), "=&v"(t)
+        : "v"(alpha));
+    acc[r] = v;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
+  using C = SplitCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  char* const kbuf = lds;
+  char* const vbuf = lds + C::TILE;
+  char* const xch = lds + 2 * C::TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = wave >> 1, dh = wave & 1;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int qt_raw = wg % p.n_qtiles;
+  const int bh = wg / p.n_qtiles;
+  const int hq = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int qt = p.causal ? (p.n_qtiles - 1 - qt_raw) : qt_raw;
+  const int hk = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int q0w = q0 + qh * 32;
+  const int qrow = q0w + l32;
+
+  const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab, (uint32_t)((int64_t)p.Nq * D * 2));
+  const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, kv_bytes);
+  const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, kv_bytes);
+  const float c = p.scale * kLog2e;
+
+  int kv_end = p.Nkv;
+  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
+
+  if (n_kt > 0) {
+    dma_tile<C, false>(rk, kbuf, 0, wave, lane);
+    dma_tile<C, true>(rv, vbuf, 0, wave, lane);
+  }
+  // Q[qrow, 32 cc + 16 dh + 8 h .. + 7] (B operand of S^T = K Q^T)
+  u32x4 qf[C::NQC];
+  {
+    const uint32_t row_off = (uint32_t)qrow * (uint32_t)(D * 2) + (uint32_t)(dh * 32 + h * 16);
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) qf[cc] = buf_load16(rq, row_off + (uint32_t)(cc * 64));
+  }
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const int klim = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
+
+  // K fragment: row l32, 16-byte chunk 4 cc + 2 dh + h = 8 (cc/2) + low,
+  // low = 4 (cc%2) + 2 dh + h; the swizzle XORs the low three bits only.
+  const int kx = k_swz(l32);
+  const uint32_t kbase0 = (uint32_t)(l32 * C::RP + (((2 * dh + h) ^ kx) << 4));
+  const uint32_t kbase1 = (uint32_t)(l32 * C::RP + (((4 + 2 * dh + h) ^ kx) << 4));
+  // V fragment (transposing read): row 16 s16 + 4 h + r16/4 (+ 8), columns
+  // 64 db + 32 dh + 16 (g16 & 1) + 4 (r16 & 3) .. + 3, i.e. 16-byte chunk
+  // 8 db + (4 dh + 2 (g16 & 1) + (r16 & 3) / 2)
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int vrow0 = 4 * h + (r16 >> 2);
+  const int vlow = 4 * dh + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const uint32_t vbase = (uint32_t)(vrow0 * C::RP + ((vlow ^ v_swz(vrow0)) << 4) + ((r16 & 1) << 3));
+  // partial-S exchange slots: wave w writes [w][j][lane] (16 B per lane, j = 0..3)
+  char* const xmine = xch + wave * 4096 + lane * 16;
+  const char* const xpeer = xch + (wave ^ 1) * 4096 + lane * 16;
+
+  if (n_kt > 0) {
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // ---- partial S^T over this wave's D/2 columns (chunks 2cc + dh) -------------
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) {
+      const uint32_t off = ((cc & 1) ? kbase1 : kbase0) + (uint32_t)((cc >> 1) * 128);
+      s = mfma_bf16(lds_load16(kbuf, off), qf[cc], s);
+      // bound how far the scheduler hoists fragment loads (registers)
+      if ((cc & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    // (float sub-vectors, not per-element bit casts: this compiler collapses
+    // bit-cast elements of an MFMA result vector onto element 0)
+    *reinterpret_cast<f32x4*>(xmine) = __builtin_shufflevector(s, s, 0, 1, 2, 3);
+    *reinterpret_cast<f32x4*>(xmine + 1024) = __builtin_shufflevector(s, s, 4, 5, 6, 7);
+    *reinterpret_cast<f32x4*>(xmine + 2048) = __builtin_shufflevector(s, s, 8, 9, 10, 11);
+    *reinterpret_cast<f32x4*>(xmine + 3072) = __builtin_shufflevector(s, s, 12, 13, 14, 15);
+    wait_vmem_all();   // V(kt) resident
+    __syncthreads();   // K buffer free, partials written, V(kt) visible
+    if (kt + 1 < n_kt) dma_tile<C, false>(rk, kbuf, kt + 1, wave, lane);
+
+    // ---- S^T = own partial + peer partial --------------------------------------
+    {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(xpeer);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(xpeer + 1024);
+      const f32x4 o2 = *reinterpret_cast<const f32x4*>(xpeer + 2048);
+      const f32x4 o3 = *reinterpret_cast<const f32x4*>(xpeer + 3072);
+      const f32x8 lo = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f32x8 hi = __builtin_shufflevector(o2, o3, 0, 1, 2, 3, 4, 5, 6, 7);
+      s += __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+
+    // scale first (any sign of scale is allowed), then mask
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] *= c;
+    const int key0 = kt * C::BC;
+    if ((key0 + C::BC > p.Nkv) || (p.causal && key0 + C::BC - 1 > q0w + p.kv_off)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        s[r] = key <= klim ? s[r] : -INFINITY;
+      }
+    }
+
+    // ---- online softmax (identical in both waves of a pair) -------------------------
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    const float mrow = fmaxf(mx, xor32(mx));  // base-2 units
+    if (__builtin_amdgcn_ballot_w64(mrow > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mrow);
+      const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) scale_acc(acc[db], alpha);
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
+    u32x4 pf[2];
+    float ls = l_run;
+#pragma unroll
+    for (int s16 = 0; s16 < 2; ++s16) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = exp2_fast(s[8 * s16 + i] + mneg);
+      pf[s16].x = pack_bf16x2(e[0], e[1]);
+      pf[s16].y = pack_bf16x2(e[2], e[3]);
+      pf[s16].z = pack_bf16x2(e[4], e[5]);
+      pf[s16].w = pack_bf16x2(e[6], e[7]);
+      ls += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+    l_run = ls;
+
+    // ---- O^T[D/2 rows] += V^T P^T ------------------------------------------------------
+#pragma unroll
+    for (int s16 = 0; s16 < 2; ++s16) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const uint32_t a0 = vbase + (uint32_t)(s16 * 16 * C::RP + db * 128);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0 + 8 * C::RP));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        acc[db] = mfma_bf16(u32x4{l2.x, l2.y, h2.x, h2.y}, pf[s16], acc[db]);
+        if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmem_all();   // K(kt+1) resident
+    __syncthreads();   // V buffer free, exchange area read, K(kt+1) visible
+    if (kt + 1 < n_kt) dma_tile<C, true>(rv, vbuf, kt + 1, wave, lane);
+  }
+
+  // ---- epilogue: this wave's 32-column blocks 2db + dh; LSE from the dh = 0 wave --
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qrow < p.Nq) {
+    const int64_t orow = q_slab + (int64_t)qrow * D + dh * 32;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 64 + 8 * g + 4 * h;
+        u32x2 pk;
+        pk.x = pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
+        pk.y = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d) = pk;
+      }
+    }
+    if (p.lse != nullptr && dh == 0 && h == 0)
+      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
+          l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_splitd(const FwdParams& p0, hipStream_t stream) {
+  using C = SplitCfg<D>;
+  FwdParams p = p0;
+  p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
+  const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
+  if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  p.total_wg = (int)total;
+  hipLaunchKernelGGL((attn_fwd_splitd_kernel<D>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+LaunchFn splitd_launcher(int elt, int D) {
+  if (elt != ELT_BF16) return nullptr;
+  switch (D) {
+    case 320: return &launch_splitd<320>;
+    case 384: return &launch_splitd<384>;
+    case 448: return &launch_splitd<448>;
+    case 512: return &launch_splitd<512>;
+    case 576: return &launch_splitd<576>;
+    case 640: return &launch_splitd<640>;
+    case 704: return &launch_splitd<704>;
+    case 768: return &launch_splitd<768>;
+    case 832: return &launch_splitd<832>;
+    case 896: return &launch_splitd<896>;
+    case 960: return &launch_splitd<960>;
+    case 1024: return &launch_splitd<1024>;
+    default: return nullptr;
+  }
+}
 
 }  // namespace attn

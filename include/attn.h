@@ -34,10 +34,11 @@
  *  reduction order) -- ZYFA article, "The details that make it
  *  production-grade" (determinism; LSE lets key-range results merge).
  *
- *  Supported sizes: B, Hq, Hkv, Nq, Nkv >= 1; D a multiple of 32 in
- *    [32, 256] for every dtype, and additionally D in [288, 1024] (multiple of
- *    32) for ATTN_BF16 via the split-D kernels; each (batch, head) slab of q,
- *    k, v and o must be smaller than 2^31 bytes; B*Hq*ceil(Nq/64) < 2^31.
+ *  Supported sizes: B, Hq, Hkv, Nq, Nkv >= 1.  Head dim D: ATTN_BF16 any
+ *    multiple of 32 in [32, 256] or any multiple of 64 in [320, 1024] (the
+ *    split-D kernels); ATTN_F32 a multiple of 32 in [32, 128]; fp8 a multiple
+ *    of 64 in [64, 256].  Each (batch, head) slab of q, k, v and o must be
+ *    smaller than 2^31 bytes; B*Hq*ceil(Nq/32) < 2^31.
  *
  * Ownership, synchronisation and errors
  * -------------------------------------

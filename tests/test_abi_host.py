@@ -65,7 +65,7 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(D=48), dict(D=1056), dict(D=2048),
+    dict(D=48), dict(D=1056), dict(D=2048), dict(D=288), dict(D=352),
     dict(D=256, dtype=A.ATTN_F32), dict(D=96, dtype=A.ATTN_FP8_E4M3), dict(D=512, dtype=A.ATTN_FP8_E4M3),
     dict(D=512, dtype=A.ATTN_F32),
     dict(Nkv=(1 << 31) // 256, D=128),            # K slab reaches 2^31 bytes

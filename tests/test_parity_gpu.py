@@ -133,6 +133,39 @@ def test_small_parity(case):
     full_parity(Workload("small", B, Hq, Hkv, Nq, Nkv, D, causal, dt, seed=sum(case[:6])))
 
 
+SPLITD_SMALL = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal): ragged tails over several 64-row query
+    # tiles and 32-key tiles, GQA, causal with Nq < Nkv and Nq > Nkv
+    (1, 2, 1, 150, 170, 320, False),
+    (1, 2, 2, 150, 170, 320, True),
+    (1, 4, 2, 97, 130, 512, True),
+    (2, 2, 2, 64, 33, 512, False),
+    (1, 2, 1, 130, 90, 768, True),
+    (1, 2, 2, 70, 200, 1024, False),
+    (1, 2, 2, 129, 129, 1024, True),
+    (1, 1, 1, 1, 1, 640, False),
+]
+
+
+@pytest.mark.parametrize("case", SPLITD_SMALL, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nkv{}_D{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_splitd_small_parity(case):
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    full_parity(Workload("splitd", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", value_scale=0.5, seed=D + Nq))
+
+
+def test_splitd_scale_variants():
+    for sc in (0.0, -0.05):
+        w = Workload("sdscale", 1, 2, 1, 80, 100, 512, True, "bf16", value_scale=0.5, seed=4)
+        inp = make_inputs(w)
+        q, k, v = (t.cuda() for t in inp)
+        o, lse = A.fwd(q, k, v, causal=True, scale=sc)
+        torch.cuda.synchronize()
+        qq, kk, vv = oracle_inputs(w, inp)
+        Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref)
+
+
 FP8_SMALL = [
     (1, 2, 2, 300, 333, 128, False),
     (1, 4, 2, 300, 333, 128, True),
@@ -225,6 +258,7 @@ def sampled_parity(w, n_heads=3, n_rows=48, seed=0):
     note(f"{w.name}: worst sampled max|dO| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("name", ["prefill_causal_bf16", "gqa_causal_bf16", "gqa_cross_bf16", "fp8_outlier"])
+@pytest.mark.parametrize("name", ["prefill_causal_bf16", "gqa_causal_bf16", "gqa_cross_bf16", "fp8_outlier",
+                                  "splitd_bf16_d320", "splitd_bf16_d512", "splitd_bf16_d768", "splitd_bf16_d1024"])
 def test_full_size_sampled(name):
     sampled_parity(WORKLOADS[name])
