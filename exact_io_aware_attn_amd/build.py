@@ -29,6 +29,9 @@ COMMON_FLAGS = [
     "-Wno-unused-function",
     # no packed-fp32 instructions are generated (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # NaN inputs are outside the ABI's contract; without this, every fmaxf on
+    # an MFMA result is preceded by a canonicalising v_max (IEEE mode)
+    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -1,0 +1,96 @@
+// attn_dma.h -- direct-to-LDS K/V tile streaming shared by the bf16 kernels
+// on gfx950: buffer descriptors in scalar registers, XOR swizzles matched to
+// the 64-bank LDS, per-lane load offsets and the loads themselves.
+#pragma once
+
+#include "attn_common.h"
+
+namespace attn {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// XOR swizzles on the 16-byte chunk index of a row.  gfx950's LDS serves
+// 256 bytes (64 banks) per clock, i.e. 16 lanes of a 16-byte read or 32
+// lanes of an 8-byte read per phase, so a phase is conflict-free when its
+// lanes touch 16 distinct chunks modulo 16.  K fragment reads put rows
+// 0..15 in one phase: chunk ^ (row & 15).  Transposing V reads put 4 rows x
+// 4 chunks (two 16-lane groups) in one phase: chunk ^ 4 (row & 3).  Both
+// need 16 chunks per row (D a multiple of 128); D = 64 rows have 8 chunks and
+// use the 8-wide forms (2-way conflicts remain there).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return row & (D % 128 == 0 ? 15 : 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) * (D % 128 == 0 ? 4 : 2); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, stride 0, num_records = nbytes, gfx9 raw
+// format) in scalar registers, for the inline-assembly loads below.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// The descriptor of one tile: base advanced by `off` bytes and the record
+// count reduced to what is left of the slab (0 past its end, so every load of
+// such a tile reads zeros).  Scalar arithmetic only.
+__device__ __forceinline__ i32x4 rsrc_at(i32x4 r, uint32_t off) {
+  const uint64_t a = ((uint64_t)(uint32_t)r.y << 32 | (uint32_t)r.x) + off;
+  const uint32_t n = (uint32_t)r.z;
+  const int left = max((int)n - (int)off, 0);  // slabs are < 2^31 bytes
+  i32x4 t;
+  t.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  t.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  t.z = __builtin_amdgcn_readfirstlane(left);
+  t.w = r.w;
+  return t;
+}
+
+// Per-lane byte offsets (within one tile) of the direct-to-LDS loads of a K
+// (IS_V = false) or V tile.  Wave `wave` fills DMA_WAVE consecutive 1 KiB
+// blocks of the LDS tile; lane l writes bytes [16 l, 16 l + 16) of a block,
+// so the global chunk it fetches is the one the swizzle places there.
+template <typename C, bool IS_V>
+__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[C::DMA_WAVE], int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::DMA_WAVE; ++j) {
+    const int o = (wave * C::DMA_WAVE + j) * 1024 + lane * 16;
+    const int row = o / C::RP;
+    const int pc = (o % C::RP) >> 4;
+    const int gc = pc ^ (IS_V ? v_swz<C::D>(row) : k_swz<C::D>(row));
+    voff[j] = (uint32_t)(row * C::RP + (gc << 4));
+  }
+}
+
+// Issue the direct-to-LDS loads of one tile (descriptor `rsrc`, positioned at
+// the tile) into LDS byte address `lds_tile`.  M0 holds each 1 KiB block's LDS
+// address.  Offsets at or past num_records read as zero.
+template <typename C>
+__device__ __forceinline__ void dma_tile(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[C::DMA_WAVE],
+                                         int wave) {
+#pragma unroll
+  for (int j = 0; j < C::DMA_WAVE; ++j) {
+    const uint32_t lds_addr = lds_tile + (uint32_t)((wave * C::DMA_WAVE + j) * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff[j]), "s"(rsrc), "s"(lds_addr)
+        : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+}  // namespace attn

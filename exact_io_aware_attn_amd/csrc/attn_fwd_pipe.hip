@@ -20,10 +20,8 @@
 //    from inline assembly so that the compiler's own wait insertion, which
 //    cannot tell the two buffers apart, does not stall every LDS read on
 //    them; the kernel waits for them explicitly before its barrier.
-//  * LDS layouts are unpadded with XOR swizzles on 16-byte chunks: K rows use
-//    chunk ^ (row & 7), so the 8 lanes of an LDS phase read 8 distinct bank
-//    groups; V rows use chunk ^ 2*(row & 3), matching the 4-row x 32-byte
-//    footprint of each 16-lane group of the transposing LDS read.
+//  * LDS layouts are unpadded with XOR swizzles on 16-byte chunks (see
+//    k_swz / v_swz): every LDS read phase touches distinct banks.
 //  * V is never transposed in registers: ds_read_b64_tr_b16 returns, for
 //    each lane, four consecutive keys of one head-dim column, which is
 //    exactly the A operand of O^T += V^T P^T.
@@ -37,6 +35,7 @@
 //    fp32 accumulators hold as well as values <= 1; O/l and m + log2(l) are
 //    unchanged, so the result is still exact.
 #include "attn_common.h"
+#include "attn_dma.h"
 #include "attn_launch.h"
 
 namespace attn {
@@ -47,77 +46,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-template <int D, int NW, int QB>
+template <int D_, int NW, int QB>
 struct PipeCfg {
+  static constexpr int D = D_;
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int NT = NW * 64;            // threads per work-group
   static constexpr int QW = QB * 32;            // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per work-group
-  static constexpr int RP = D * 2;              // LDS row pitch (bytes)
+  static constexpr int RP = D_ * 2;             // LDS row pitch (bytes)
   static constexpr int TILE = BC * RP;          // bytes of one K or V tile
   static constexpr int DMA_TILE = TILE / 1024;  // wave-wide 16 B/lane loads per tile
   static constexpr int DMA_WAVE = DMA_TILE / NW;
-  static constexpr int NDB = D / 32;            // 32-row blocks of O^T
-  static constexpr int NQC = D / 16;            // 16-wide d chunks of the QK^T contraction
+  static constexpr int NDB = D_ / 32;           // 32-row blocks of O^T
+  static constexpr int NQC = D_ / 16;           // 16-wide d chunks of the QK^T contraction
   static constexpr int NKB = BC / 32;           // 32-key blocks of S^T per tile
   static constexpr int LDS = 4 * TILE;          // K0, K1, V0, V1
-  static_assert(D % 64 == 0, "D must be a multiple of 64");
+  static_assert(D_ % 64 == 0, "D must be a multiple of 64");
   static_assert(DMA_TILE % NW == 0, "tile must split evenly over the waves");
 };
-
-// XOR swizzles on the 16-byte chunk index of a row (both stay inside an
-// aligned group of 8 chunks, so any D that is a multiple of 64 works).
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (base, stride 0, num_records = nbytes, gfx9 raw
-// format) in scalar registers, for the inline-assembly loads below.
-__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-// Issue the direct-to-LDS loads of one K (IS_V = false) or V tile.  Each
-// wave fills DMA_WAVE consecutive 1 KiB blocks; lane l writes bytes
-// [16 l, 16 l + 16) of a block (M0 holds the block's LDS address), so the
-// global chunk it fetches is the one the swizzle places there.  Offsets at or
-// past num_records read as zero.
-template <typename C, bool IS_V>
-__device__ __forceinline__ void dma_tile(i32x4 rsrc, const char* dst, int kt, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < C::DMA_WAVE; ++j) {
-    const int blk = wave * C::DMA_WAVE + j;
-    const int o = blk * 1024 + lane * 16;
-    const int row = o / C::RP;
-    const int pc = (o % C::RP) >> 4;
-    const int gc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
-    const uint32_t voff = (uint32_t)(kt * C::BC + row) * (uint32_t)C::RP + (uint32_t)(gc << 4);
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(dst + blk * 1024);
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds"
-        :
-        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-        : "memory", "m0");
-  }
-}
-
-__device__ __forceinline__ void wait_vmem_all() {
-  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
 
 template <int D, int NW, int QB>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
@@ -127,6 +73,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   char* const kbuf1 = lds + C::TILE;
   char* const vbuf0 = lds + 2 * C::TILE;
   char* const vbuf1 = lds + 3 * C::TILE;
+  // LDS byte address of the buffer block (the M0 operand of the loads)
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  const uint32_t lk0 = lds_base, lk1 = lds_base + C::TILE;
+  const uint32_t lv0 = lds_base + 2 * C::TILE, lv1 = lds_base + 3 * C::TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,9 +111,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
   // ---- prologue loads: K0, V0 (LDS), Q (registers) -------------------------------
+  uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
+  dma_offsets<C, false>(dk, wave, lane);
+  dma_offsets<C, true>(dv, wave, lane);
   if (n_kt > 0) {
-    dma_tile<C, false>(rk, kbuf0, 0, wave, lane);
-    dma_tile<C, true>(rv, vbuf0, 0, wave, lane);
+    dma_tile<C>(rk, lk0, dk, wave);
+    dma_tile<C>(rv, lv0, dv, wave);
   }
   u32x4 qf[QB][C::NQC];
 #pragma unroll
@@ -188,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   // K fragment (A operand of S^T = K Q^T): row l32 (+32 kb), chunk 2cc + h
   uint32_t koff[C::NQC];
 #pragma unroll
-  for (int cc = 0; cc < C::NQC; ++cc) koff[cc] = (uint32_t)(l32 * C::RP + (((2 * cc + h) ^ k_swz(l32)) << 4));
+  for (int cc = 0; cc < C::NQC; ++cc) koff[cc] = (uint32_t)(l32 * C::RP + (((2 * cc + h) ^ k_swz<D>(l32)) << 4));
   // V fragment (A operand of O^T += V^T P^T) via the transposing read: lane r
   // of each 16-lane group addresses row kbase + r/4, columns dbase + 4(r%4)..+3
   const int g16 = lane >> 4, r16 = lane & 15;
@@ -197,7 +151,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   for (int db = 0; db < C::NDB; ++db) {
     const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
     const int row = 4 * h + (r16 >> 2);  // + 16 s16 (+ 8): multiples of 4 keep row & 3
-    voff[db] = (uint32_t)(row * C::RP + ((chunk ^ v_swz(row)) << 4) + ((r16 & 1) << 3));
+    voff[db] = (uint32_t)(row * C::RP + ((chunk ^ v_swz<D>(row)) << 4) + ((r16 & 1) << 3));
   }
   // last visible key of this lane's query row in each block
   int klim[QB];
@@ -217,8 +171,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
     const char* const kb_cur = odd ? kbuf1 : kbuf0;
     const char* const vb_cur = odd ? vbuf1 : vbuf0;
     if (kt + 1 < n_kt) {
-      dma_tile<C, false>(rk, odd ? kbuf0 : kbuf1, kt + 1, wave, lane);
-      dma_tile<C, true>(rv, odd ? vbuf0 : vbuf1, kt + 1, wave, lane);
+      const uint32_t toff = (uint32_t)((kt + 1) * C::TILE);
+      dma_tile<C>(rsrc_at(rk, toff), odd ? lk0 : lk1, dk, wave);
+      dma_tile<C>(rsrc_at(rv, toff), odd ? lv0 : lv1, dv, wave);
     }
 
     // ---- S^T = K Q^T ------------------------------------------------------------
@@ -227,13 +182,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) s[qb][kb] = f32x16{};
+    // K fragments of a whole 32-key block are read before its MFMAs, and the
+    // next block's reads are issued before the current block's MFMAs, so LDS
+    // latency overlaps the matrix work instead of stalling each instruction.
+    u32x4 kfa[C::NQC], kfb[C::NQC];
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) kfa[cc] = lds_load16(kb_cur, koff[cc]);
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
+      u32x4(&cur)[C::NQC] = (kb & 1) ? kfb : kfa;
+      u32x4(&nxt)[C::NQC] = (kb & 1) ? kfa : kfb;
+      if (kb + 1 < C::NKB) {
+#pragma unroll
+        for (int cc = 0; cc < C::NQC; ++cc) nxt[cc] = lds_load16(kb_cur, koff[cc] + (uint32_t)((kb + 1) * 32 * C::RP));
+      }
 #pragma unroll
       for (int cc = 0; cc < C::NQC; ++cc) {
-        const u32x4 kf = lds_load16(kb_cur, koff[cc] + (uint32_t)(kb * 32 * C::RP));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(kf, qf[qb][cc], s[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(cur[cc], qf[qb][cc], s[qb][kb]);
       }
     }
 
@@ -255,11 +221,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
     u32x4 pf[QB][2 * C::NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // one running chain, so the compiler forms v_max3 (two scores each)
       float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
       const float mrow = fmaxf(mx, xor32(mx)) * c;  // scaled (base-2) units
       if (__builtin_amdgcn_ballot_w64(mrow > m_run[qb] + kTau) != 0) {
         // rows that have seen no visible key yet keep m = -inf; exp2 of
@@ -289,17 +256,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
     }
 
     // ---- O^T += V^T P^T ---------------------------------------------------------------
-#pragma unroll
-    for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+    // V fragments: the reads of 16-key sub-block s16+1 are issued before the
+    // MFMAs of sub-block s16.
+    auto vread = [&](int s16, u32x4 (&vf)[C::NDB]) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
         const uint32_t a0 = voff[db] + (uint32_t)(s16 * 16 * C::RP);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0 + 8 * C::RP));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 vf = {l2.x, l2.y, h2.x, h2.y};
+        vf[db] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    };
+    u32x4 vfa[C::NDB], vfb[C::NDB];
+    vread(0, vfa);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(vf, pf[qb][s16], acc[qb][db]);
+    for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+      u32x4(&cur)[C::NDB] = (s16 & 1) ? vfb : vfa;
+      u32x4(&nxt)[C::NDB] = (s16 & 1) ? vfa : vfb;
+      if (s16 + 1 < 2 * C::NKB) vread(s16 + 1, nxt);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(cur[db], pf[qb][s16], acc[qb][db]);
       }
     }
 

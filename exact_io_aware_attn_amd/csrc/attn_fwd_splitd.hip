@@ -34,6 +34,7 @@
 //    work-group ranges and heaviest-first causal order as in the other
 //    kernels.
 #include "attn_common.h"
+#include "attn_dma.h"
 #include "attn_launch.h"
 
 namespace attn {
@@ -44,69 +45,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-template <int D>
+template <int D_>
 struct SplitCfg {
+  static constexpr int D = D_;
   static constexpr int NW = 4;                     // (query half) x (head-dim half)
   static constexpr int NT = NW * 64;
   static constexpr int BR = 64;                    // query rows per work-group
   static constexpr int BC = 32;                    // keys per tile
-  static constexpr int DH = D / 2;                 // head-dim columns per wave
-  static constexpr int RP = D * 2;                 // LDS row pitch (bytes)
+  static constexpr int DH = D_ / 2;                // head-dim columns per wave
+  static constexpr int RP = D_ * 2;                // LDS row pitch (bytes)
   static constexpr int TILE = BC * RP;             // one K or V tile
   static constexpr int DMA_WAVE = TILE / 1024 / NW;
   static constexpr int NQC = DH / 16;              // QK^T k-steps per wave (16-col chunks 2cc + dh)
   static constexpr int NDB = DH / 32;              // 32-row blocks of O^T per wave (blocks 2db + dh)
   static constexpr int XCH = NW * 64 * 16 * 4;     // partial-S exchange area
   static constexpr int LDS = 2 * TILE + XCH;
-  static_assert(D % 64 == 0, "D must be a multiple of 64");
+  static_assert(D_ % 64 == 0, "D must be a multiple of 64");
   static_assert((TILE / 1024) % NW == 0, "tile must split evenly over the waves");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
-
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
-
-__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-// Direct-to-LDS loads of one tile (see the D <= 128 kernel for the layout):
-// wave `wave` fills DMA_WAVE consecutive 1 KiB blocks, lane l writes bytes
-// [16 l, 16 l + 16) of each block.  Loads are issued from inline assembly so
-// the compiler does not stall LDS reads of the other buffer on them.
-template <typename C, bool IS_V>
-__device__ __forceinline__ void dma_tile(i32x4 rsrc, const char* dst, int kt, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < C::DMA_WAVE; ++j) {
-    const int blk = wave * C::DMA_WAVE + j;
-    const int o = blk * 1024 + lane * 16;
-    const int row = o / C::RP;
-    const int pc = (o % C::RP) >> 4;
-    const int gc = pc ^ (IS_V ? v_swz(row) : k_swz(row));
-    const uint32_t voff = (uint32_t)(kt * C::BC + row) * (uint32_t)C::RP + (uint32_t)(gc << 4);
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(dst + blk * 1024);
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds"
-        :
-        : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-        : "memory", "m0");
-  }
-}
-
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // acc *= alpha with every element kept in an accumulation register (AGPR).
 // Written as C++, the multiply would make the register allocator hold the
@@ -133,6 +92,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   char* const kbuf = lds;
   char* const vbuf = lds + C::TILE;
   char* const xch = lds + 2 * C::TILE;
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  const uint32_t lk = lds_base, lv = lds_base + C::TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,9 +126,12 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
+  uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
+  dma_offsets<C, false>(dk, wave, lane);
+  dma_offsets<C, true>(dv, wave, lane);
   if (n_kt > 0) {
-    dma_tile<C, false>(rk, kbuf, 0, wave, lane);
-    dma_tile<C, true>(rv, vbuf, 0, wave, lane);
+    dma_tile<C>(rk, lk, dk, wave);
+    dma_tile<C>(rv, lv, dv, wave);
   }
   // Q[qrow, 32 cc + 16 dh + 8 h .. + 7] (B operand of S^T = K Q^T)
   u32x4 qf[C::NQC];
@@ -182,18 +147,27 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.0f;
   const int klim = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
 
-  // K fragment: row l32, 16-byte chunk 4 cc + 2 dh + h = 8 (cc/2) + low,
-  // low = 4 (cc%2) + 2 dh + h; the swizzle XORs the low three bits only.
-  const int kx = k_swz(l32);
-  const uint32_t kbase0 = (uint32_t)(l32 * C::RP + (((2 * dh + h) ^ kx) << 4));
-  const uint32_t kbase1 = (uint32_t)(l32 * C::RP + (((4 + 2 * dh + h) ^ kx) << 4));
+  // K fragment: row l32, 16-byte chunk 4 cc + 2 dh + h.  The swizzle XORs
+  // the low KB bits (KB = 3 or 4), so with G = 2^KB / 4 the address is
+  // kbase[cc % G] + (cc / G) * 2^KB * 16.
+  constexpr int KG = (D % 128 == 0) ? 4 : 2;
+  const int kx = k_swz<D>(l32);
+  uint32_t kbase[KG];
+#pragma unroll
+  for (int i = 0; i < KG; ++i) kbase[i] = (uint32_t)(l32 * C::RP + (((4 * i + 2 * dh + h) ^ kx) << 4));
   // V fragment (transposing read): row 16 s16 + 4 h + r16/4 (+ 8), columns
   // 64 db + 32 dh + 16 (g16 & 1) + 4 (r16 & 3) .. + 3, i.e. 16-byte chunk
-  // 8 db + (4 dh + 2 (g16 & 1) + (r16 & 3) / 2)
+  // 8 db + vlow with vlow = 4 dh + 2 (g16 & 1) + (r16 & 3) / 2; with
+  // VG = 2^VB / 8 (VB = swizzle width in bits) the address is
+  // vbase[db % VG] + (db / VG) * 2^VB * 16.
+  constexpr int VG = (D % 128 == 0) ? 2 : 1;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int vrow0 = 4 * h + (r16 >> 2);
   const int vlow = 4 * dh + 2 * (g16 & 1) + ((r16 & 3) >> 1);
-  const uint32_t vbase = (uint32_t)(vrow0 * C::RP + ((vlow ^ v_swz(vrow0)) << 4) + ((r16 & 1) << 3));
+  uint32_t vbase[VG];
+#pragma unroll
+  for (int i = 0; i < VG; ++i)
+    vbase[i] = (uint32_t)(vrow0 * C::RP + (((8 * i + vlow) ^ v_swz<D>(vrow0)) << 4) + ((r16 & 1) << 3));
   // partial-S exchange slots: wave w writes [w][j][lane] (16 B per lane, j = 0..3)
   char* const xmine = xch + wave * 4096 + lane * 16;
   const char* const xpeer = xch + (wave ^ 1) * 4096 + lane * 16;
@@ -208,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < C::NQC; ++cc) {
-      const uint32_t off = ((cc & 1) ? kbase1 : kbase0) + (uint32_t)((cc >> 1) * 128);
+      const uint32_t off = kbase[cc % KG] + (uint32_t)((cc / KG) * KG * 64);
       s = mfma_bf16(lds_load16(kbuf, off), qf[cc], s);
       // bound how far the scheduler hoists fragment loads (registers)
       if ((cc & 7) == 7) __builtin_amdgcn_sched_barrier(0);
@@ -221,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     *reinterpret_cast<f32x4*>(xmine + 3072) = __builtin_shufflevector(s, s, 12, 13, 14, 15);
     wait_vmem_all();   // V(kt) resident
     __syncthreads();   // K buffer free, partials written, V(kt) visible
-    if (kt + 1 < n_kt) dma_tile<C, false>(rk, kbuf, kt + 1, wave, lane);
+    if (kt + 1 < n_kt) dma_tile<C>(rsrc_at(rk, (uint32_t)((kt + 1) * C::TILE)), lk, dk, wave);
 
     // ---- S^T = own partial + peer partial --------------------------------------
     {
@@ -249,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     // ---- online softmax (identical in both waves of a pair) -------------------------
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
     const float mrow = fmaxf(mx, xor32(mx));  // base-2 units
     if (__builtin_amdgcn_ballot_w64(mrow > m_run + kTau) != 0) {
       const float m_new = fmaxf(m_run, mrow);
@@ -280,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     for (int s16 = 0; s16 < 2; ++s16) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const uint32_t a0 = vbase + (uint32_t)(s16 * 16 * C::RP + db * 128);
+        const uint32_t a0 = vbase[db % VG] + (uint32_t)(s16 * 16 * C::RP + (db / VG) * VG * 128);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0 + 8 * C::RP));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -290,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     }
     wait_vmem_all();   // K(kt+1) resident
     __syncthreads();   // V buffer free, exchange area read, K(kt+1) visible
-    if (kt + 1 < n_kt) dma_tile<C, true>(rv, vbuf, kt + 1, wave, lane);
+    if (kt + 1 < n_kt) dma_tile<C>(rsrc_at(rv, (uint32_t)((kt + 1) * C::TILE)), lv, dv, wave);
   }
 
   // ---- epilogue: this wave's 32-column blocks 2db + dh; LSE from the dh = 0 wave --
