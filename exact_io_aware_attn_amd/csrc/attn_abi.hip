@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
 

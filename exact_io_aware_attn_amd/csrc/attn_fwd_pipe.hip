@@ -46,9 +46,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
-template <int D_, int NW, int QB>
+template <int D_, int NW_, int NBUF_>
 struct PipeCfg {
   static constexpr int D = D_;
+  static constexpr int NW = NW_;                // waves per work-group
+  static constexpr int NBUF = NBUF_;            // K/V tiles resident (ring)
+  static constexpr int QB = 1;                  // 32-row query blocks per wave
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int NT = NW * 64;            // threads per work-group
   static constexpr int QW = QB * 32;            // query rows per wave
@@ -60,24 +63,25 @@ struct PipeCfg {
   static constexpr int NDB = D_ / 32;           // 32-row blocks of O^T
   static constexpr int NQC = D_ / 16;           // 16-wide d chunks of the QK^T contraction
   static constexpr int NKB = BC / 32;           // 32-key blocks of S^T per tile
-  static constexpr int LDS = 4 * TILE;          // K0, K1, V0, V1
+  static constexpr int LDS = 2 * NBUF * TILE;   // K ring, V ring
+  // s_waitcnt immediate for vmcnt(n): the loads of the NBUF-2 tiles issued
+  // after a given tile may stay in flight (expcnt, lgkmcnt at their maxima)
+  static constexpr int LATER = (NBUF - 2) * 2 * DMA_WAVE;
+  static constexpr int WAIT_LATER = 0x0F70 | (LATER & 15) | ((LATER >> 4) << 14);
+  static_assert(NBUF >= 2 && LATER < 64, "ring depth");
   static_assert(D_ % 64 == 0, "D must be a multiple of 64");
   static_assert(DMA_TILE % NW == 0, "tile must split evenly over the waves");
 };
 
-template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
-  using C = PipeCfg<D, NW, QB>;
+template <int D, int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel(FwdParams p) {
+  using C = PipeCfg<D, NW, NBUF>;
+  constexpr int QB = C::QB;
+  // LDS: K ring (NBUF tiles) then V ring (NBUF tiles)
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
-  char* const kbuf0 = lds;
-  char* const kbuf1 = lds + C::TILE;
-  char* const vbuf0 = lds + 2 * C::TILE;
-  char* const vbuf1 = lds + 3 * C::TILE;
-  // LDS byte address of the buffer block (the M0 operand of the loads)
+  // LDS byte address of the buffer (the M0 operand of the loads)
   const uint32_t lds_base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
-  const uint32_t lk0 = lds_base, lk1 = lds_base + C::TILE;
-  const uint32_t lv0 = lds_base + 2 * C::TILE, lv1 = lds_base + 3 * C::TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,14 +114,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
-  // ---- prologue loads: K0, V0 (LDS), Q (registers) -------------------------------
+  // ---- prologue loads: tiles 0 .. NBUF-2 (LDS), Q (registers) --------------------
   uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
   dma_offsets<C, false>(dk, wave, lane);
   dma_offsets<C, true>(dv, wave, lane);
-  if (n_kt > 0) {
-    dma_tile<C>(rk, lk0, dk, wave);
-    dma_tile<C>(rv, lv0, dv, wave);
-  }
+  auto issue_tile = [&](int t, int slot) {
+    const uint32_t toff = (uint32_t)(t * C::TILE);
+    dma_tile<C>(rsrc_at(rk, toff), lds_base + (uint32_t)(slot * C::TILE), dk, wave);
+    dma_tile<C>(rsrc_at(rv, toff), lds_base + (uint32_t)((NBUF + slot) * C::TILE), dv, wave);
+  };
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < n_kt) issue_tile(t, t);
   u32x4 qf[QB][C::NQC];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -161,20 +169,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
     klim[qb] = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
   }
 
-  if (n_kt > 0) {
-    wait_vmem_all();
-    __syncthreads();
-  }
-
+  int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
-    const bool odd = kt & 1;
-    const char* const kb_cur = odd ? kbuf1 : kbuf0;
-    const char* const vb_cur = odd ? vbuf1 : vbuf0;
-    if (kt + 1 < n_kt) {
-      const uint32_t toff = (uint32_t)((kt + 1) * C::TILE);
-      dma_tile<C>(rsrc_at(rk, toff), odd ? lk0 : lk1, dk, wave);
-      dma_tile<C>(rsrc_at(rv, toff), odd ? lv0 : lv1, dv, wave);
-    }
+    // Tile kt is resident once at most the loads of the NBUF-2 later tiles
+    // are outstanding (loads complete in order); the barrier makes every
+    // wave's loads visible and frees the slot of tile kt-1 for reloading.
+    if (kt + NBUF - 2 < n_kt)
+      __builtin_amdgcn_s_waitcnt(C::WAIT_LATER);
+    else
+      wait_vmem_all();
+    __syncthreads();
+    if (kt + NBUF - 1 < n_kt) issue_tile(kt + NBUF - 1, slot == 0 ? NBUF - 1 : slot - 1);
+    const char* const kb_cur = lds + slot * C::TILE;
+    const char* const vb_cur = lds + (NBUF + slot) * C::TILE;
+    slot = slot == NBUF - 1 ? 0 : slot + 1;
 
     // ---- S^T = K Q^T ------------------------------------------------------------
     f32x16 s[QB][C::NKB];
@@ -282,9 +290,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
       }
     }
 
-    // ---- the next tiles are resident and every wave is done with this one --------
-    wait_vmem_all();
-    __syncthreads();
   }
 
   // ---- epilogue ---------------------------------------------------------------------
@@ -313,15 +318,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) 
   }
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW, int NBUF>
 hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
-  using C = PipeCfg<D, NW, QB>;
+  using C = PipeCfg<D, NW, NBUF>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, QB>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, NBUF>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -329,8 +334,14 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
 
 LaunchFn pipe_launcher(int elt, int D) {
   if (elt != ELT_BF16) return nullptr;
-  if (D == 128) return &launch_pipe<128, 4, 1>;
-  if (D == 64) return &launch_pipe<64, 4, 1>;
+#ifndef ATTN_PIPE_NW
+#define ATTN_PIPE_NW 4
+#endif
+#ifndef ATTN_PIPE_NBUF
+#define ATTN_PIPE_NBUF 2
+#endif
+  if (D == 128) return &launch_pipe<128, ATTN_PIPE_NW, ATTN_PIPE_NBUF>;
+  if (D == 64) return &launch_pipe<64, ATTN_PIPE_NW, ATTN_PIPE_NBUF>;
   return nullptr;
 }
 
