@@ -93,4 +93,22 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// acc *= alpha with every element kept in an accumulation register (AGPR).
+// Written as C++, the multiply would make the register allocator hold the
+// loop-carried accumulators in VGPRs and copy all of them to and from AGPRs
+// on every tile (D/4 registers each way); the "a" constraint pins them.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = acc[r], t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(v), "=&v"(t)
+        : "v"(alpha));
+    acc[r] = v;
+  }
+}
+
 }  // namespace attn

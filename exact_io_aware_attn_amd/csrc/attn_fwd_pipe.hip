@@ -46,13 +46,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
-template <int D_, int NW_, int NBUF_>
+template <int D_, int NW_, int NBUF_, int BC_>
 struct PipeCfg {
   static constexpr int D = D_;
   static constexpr int NW = NW_;                // waves per work-group
   static constexpr int NBUF = NBUF_;            // K/V tiles resident (ring)
   static constexpr int QB = 1;                  // 32-row query blocks per wave
-  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int BC = BC_;                // keys per tile
+  static constexpr bool LARGE = D_ > 128;       // Q/O too large for 2 waves per SIMD
   static constexpr int NT = NW * 64;            // threads per work-group
   static constexpr int QW = QB * 32;            // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per work-group
@@ -64,18 +65,23 @@ struct PipeCfg {
   static constexpr int NQC = D_ / 16;           // 16-wide d chunks of the QK^T contraction
   static constexpr int NKB = BC / 32;           // 32-key blocks of S^T per tile
   static constexpr int LDS = 2 * NBUF * TILE;   // K ring, V ring
+  static constexpr int SW = (D_ % 128 == 0) ? 16 : 8;  // swizzle width (16-byte chunks)
+  static constexpr int LK = NQC < 8 ? NQC : 8;  // K fragments in flight (large D)
+  static constexpr int LV = NDB < 4 ? NDB : 4;  // V fragments in flight (large D)
   // s_waitcnt immediate for vmcnt(n): the loads of the NBUF-2 tiles issued
   // after a given tile may stay in flight (expcnt, lgkmcnt at their maxima)
   static constexpr int LATER = (NBUF - 2) * 2 * DMA_WAVE;
   static constexpr int WAIT_LATER = 0x0F70 | (LATER & 15) | ((LATER >> 4) << 14);
   static_assert(NBUF >= 2 && LATER < 64, "ring depth");
   static_assert(D_ % 64 == 0, "D must be a multiple of 64");
+  static_assert(BC % 32 == 0, "BC must be a multiple of 32");
   static_assert(DMA_TILE % NW == 0, "tile must split evenly over the waves");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel(FwdParams p) {
-  using C = PipeCfg<D, NW, NBUF>;
+template <int D, int NW, int NBUF, int BC>
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_fwd_pipe_kernel(FwdParams p) {
+  using C = PipeCfg<D, NW, NBUF, BC>;
   constexpr int QB = C::QB;
   // LDS: K ring (NBUF tiles) then V ring (NBUF tiles)
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
@@ -146,21 +152,27 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel
     l_run[qb] = 0.0f;
   }
 
-  // per-lane LDS byte offsets that do not change across tiles
+  // per-lane LDS byte offsets that do not change across tiles.  The swizzles
+  // XOR the low log2(SW) bits of a 16-byte chunk index, so fragment cc of K
+  // (chunk 2cc + h) sits at kbase[cc % KG] + (cc / KG) * SW * 16 and fragment
+  // db of V (chunk 4db + ...) at vbase[db % VG] + (db / VG) * SW * 16.
   // K fragment (A operand of S^T = K Q^T): row l32 (+32 kb), chunk 2cc + h
-  uint32_t koff[C::NQC];
+  constexpr int KG = C::SW / 2, VG = C::SW / 4;
+  uint32_t kbase[KG];
 #pragma unroll
-  for (int cc = 0; cc < C::NQC; ++cc) koff[cc] = (uint32_t)(l32 * C::RP + (((2 * cc + h) ^ k_swz<D>(l32)) << 4));
+  for (int i = 0; i < KG; ++i) kbase[i] = (uint32_t)(l32 * C::RP + (((2 * i + h) ^ k_swz<D>(l32)) << 4));
+  auto koff = [&](int cc) { return kbase[cc % KG] + (uint32_t)((cc / KG) * C::SW * 16); };
   // V fragment (A operand of O^T += V^T P^T) via the transposing read: lane r
   // of each 16-lane group addresses row kbase + r/4, columns dbase + 4(r%4)..+3
   const int g16 = lane >> 4, r16 = lane & 15;
-  uint32_t voff[C::NDB];
+  uint32_t vbase[VG];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  for (int i = 0; i < VG; ++i) {
+    const int chunk = i * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
     const int row = 4 * h + (r16 >> 2);  // + 16 s16 (+ 8): multiples of 4 keep row & 3
-    voff[db] = (uint32_t)(row * C::RP + ((chunk ^ v_swz<D>(row)) << 4) + ((r16 & 1) << 3));
+    vbase[i] = (uint32_t)(row * C::RP + ((chunk ^ v_swz<D>(row)) << 4) + ((r16 & 1) << 3));
   }
+  auto voff = [&](int db) { return vbase[db % VG] + (uint32_t)((db / VG) * C::SW * 16); };
   // last visible key of this lane's query row in each block
   int klim[QB];
 #pragma unroll
@@ -190,24 +202,42 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) s[qb][kb] = f32x16{};
-    // K fragments of a whole 32-key block are read before its MFMAs, and the
-    // next block's reads are issued before the current block's MFMAs, so LDS
-    // latency overlaps the matrix work instead of stalling each instruction.
-    u32x4 kfa[C::NQC], kfb[C::NQC];
+    if constexpr (!C::LARGE) {
+      // K fragments of a whole 32-key block are read before its MFMAs, and the
+      // next block's reads are issued before the current block's MFMAs, so LDS
+      // latency overlaps the matrix work instead of stalling each instruction.
+      u32x4 kfa[C::NQC], kfb[C::NQC];
 #pragma unroll
-    for (int cc = 0; cc < C::NQC; ++cc) kfa[cc] = lds_load16(kb_cur, koff[cc]);
+      for (int cc = 0; cc < C::NQC; ++cc) kfa[cc] = lds_load16(kb_cur, koff(cc));
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      u32x4(&cur)[C::NQC] = (kb & 1) ? kfb : kfa;
-      u32x4(&nxt)[C::NQC] = (kb & 1) ? kfa : kfb;
-      if (kb + 1 < C::NKB) {
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        u32x4(&cur)[C::NQC] = (kb & 1) ? kfb : kfa;
+        u32x4(&nxt)[C::NQC] = (kb & 1) ? kfa : kfb;
+        if (kb + 1 < C::NKB) {
 #pragma unroll
-        for (int cc = 0; cc < C::NQC; ++cc) nxt[cc] = lds_load16(kb_cur, koff[cc] + (uint32_t)((kb + 1) * 32 * C::RP));
+          for (int cc = 0; cc < C::NQC; ++cc) nxt[cc] = lds_load16(kb_cur, koff(cc) + (uint32_t)((kb + 1) * 32 * C::RP));
+        }
+#pragma unroll
+        for (int cc = 0; cc < C::NQC; ++cc) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(cur[cc], qf[qb][cc], s[qb][kb]);
+        }
       }
+    } else {
+      // large D: a fixed number (LK) of K fragments in flight
 #pragma unroll
-      for (int cc = 0; cc < C::NQC; ++cc) {
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const uint32_t kbo = (uint32_t)(kb * 32 * C::RP);
+        u32x4 kf[C::LK];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(cur[cc], qf[qb][cc], s[qb][kb]);
+        for (int i = 0; i < C::LK; ++i) kf[i] = lds_load16(kb_cur, koff(i) + kbo);
+#pragma unroll
+        for (int cc = 0; cc < C::NQC; ++cc) {
+          const u32x4 cur = kf[cc % C::LK];
+          if (cc + C::LK < C::NQC) kf[cc % C::LK] = lds_load16(kb_cur, koff(cc + C::LK) + kbo);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(cur, qf[qb][cc], s[qb][kb]);
+        }
       }
     }
 
@@ -241,8 +271,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel
         // (-inf) - 0 is 0 there, never (-inf) - (-inf)
         const float m_new = fmaxf(m_run[qb], mrow);
         const float alpha = exp2_fast(m_run[qb] - (m_new == -INFINITY ? 0.0f : m_new));
+        if constexpr (C::LARGE) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) acc[qb][db] *= alpha;
+          for (int db = 0; db < C::NDB; ++db) scale_acc(acc[qb][db], alpha);
+        } else {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) acc[qb][db] *= alpha;
+        }
         l_run[qb] *= alpha;
         m_run[qb] = m_new;
       }
@@ -266,27 +301,45 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel
     // ---- O^T += V^T P^T ---------------------------------------------------------------
     // V fragments: the reads of 16-key sub-block s16+1 are issued before the
     // MFMAs of sub-block s16.
-    auto vread = [&](int s16, u32x4 (&vf)[C::NDB]) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const uint32_t a0 = voff[db] + (uint32_t)(s16 * 16 * C::RP);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0 + 8 * C::RP));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        vf[db] = u32x4{l2.x, l2.y, h2.x, h2.y};
-      }
+    auto vfrag = [&](int s16, int db) {
+      const uint32_t a0 = voff(db) + (uint32_t)(s16 * 16 * C::RP);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_cur + a0 + 8 * C::RP));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2.x, l2.y, h2.x, h2.y};
     };
-    u32x4 vfa[C::NDB], vfb[C::NDB];
-    vread(0, vfa);
+    if constexpr (!C::LARGE) {
+      u32x4 vfa[C::NDB], vfb[C::NDB];
 #pragma unroll
-    for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
-      u32x4(&cur)[C::NDB] = (s16 & 1) ? vfb : vfa;
-      u32x4(&nxt)[C::NDB] = (s16 & 1) ? vfa : vfb;
-      if (s16 + 1 < 2 * C::NKB) vread(s16 + 1, nxt);
+      for (int db = 0; db < C::NDB; ++db) vfa[db] = vfrag(0, db);
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
+      for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+        u32x4(&cur)[C::NDB] = (s16 & 1) ? vfb : vfa;
+        u32x4(&nxt)[C::NDB] = (s16 & 1) ? vfa : vfb;
+        if (s16 + 1 < 2 * C::NKB) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(cur[db], pf[qb][s16], acc[qb][db]);
+          for (int db = 0; db < C::NDB; ++db) nxt[db] = vfrag(s16 + 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(cur[db], pf[qb][s16], acc[qb][db]);
+        }
+      }
+    } else {
+      // large D: a fixed number (LV) of V fragments in flight
+#pragma unroll
+      for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
+        u32x4 vf[C::LV];
+#pragma unroll
+        for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(s16, i);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const u32x4 cur = vf[db % C::LV];
+          if (db + C::LV < C::NDB) vf[db % C::LV] = vfrag(s16, db + C::LV);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(cur, pf[qb][s16], acc[qb][db]);
+        }
       }
     }
 
@@ -318,15 +371,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_pipe_kernel
   }
 }
 
-template <int D, int NW, int NBUF>
+template <int D, int NW, int NBUF, int BC>
 hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
-  using C = PipeCfg<D, NW, NBUF>;
+  using C = PipeCfg<D, NW, NBUF, BC>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, NBUF>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, NBUF, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -334,15 +387,20 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
 
 LaunchFn pipe_launcher(int elt, int D) {
   if (elt != ELT_BF16) return nullptr;
-#ifndef ATTN_PIPE_NW
-#define ATTN_PIPE_NW 4
-#endif
-#ifndef ATTN_PIPE_NBUF
-#define ATTN_PIPE_NBUF 2
-#endif
-  if (D == 128) return &launch_pipe<128, ATTN_PIPE_NW, ATTN_PIPE_NBUF>;
-  if (D == 64) return &launch_pipe<64, ATTN_PIPE_NW, ATTN_PIPE_NBUF>;
-  return nullptr;
+  switch (D) {
+    // two work-groups of 4 waves per CU, 64-key tiles, double-buffered
+    case 64: return &launch_pipe<64, 4, 2, 64>;
+    case 128: return &launch_pipe<128, 4, 2, 64>;
+    // one work-group per CU: a wave holds Q[32, D] (D/8 VGPRs) and O (D/4
+    // accumulators), 32-key tiles, double-buffered
+    case 192: return &launch_pipe<192, 4, 2, 32>;
+    case 256: return &launch_pipe<256, 4, 2, 32>;
+    case 320: return &launch_pipe<320, 4, 2, 32>;
+    case 384: return &launch_pipe<384, 4, 2, 32>;
+    case 448: return &launch_pipe<448, 4, 2, 32>;
+    case 512: return &launch_pipe<512, 4, 2, 32>;
+    default: return nullptr;
+  }
 }
 
 }  // namespace attn

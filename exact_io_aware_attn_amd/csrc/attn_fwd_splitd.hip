@@ -67,24 +67,6 @@ struct SplitCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// acc *= alpha with every element kept in an accumulation register (AGPR).
-// Written as C++, the multiply would make the register allocator hold the
-// loop-carried accumulators in VGPRs and copy all of them to and from AGPRs
-// on every tile (D/4 registers each way); the "a" constraint pins them.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float v = acc[r], t;
-    asm volatile(
-        "v_accvgpr_read_b32 %1, %0\n\t"
-        "v_mul_f32 %1, %1, %2\n\t"
-        "v_accvgpr_write_b32 %0, %1"
-        : "+a"(v), "=&v"(t)
-        : "v"(alpha));
-    acc[r] = v;
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   using C = SplitCfg<D>;
