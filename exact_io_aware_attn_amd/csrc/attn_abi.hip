@@ -57,7 +57,8 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   if (B * Hq * ((Nq + 31) / 32) >= lim)
     return fail(ATTN_ERR_UNSUPPORTED, "grid too large: B*Hq*ceil(Nq/32) must be < 2^31");
 
-  // The direct-to-LDS kernel (bf16, D a multiple of 64 up to 512) folds the
+  // The direct-to-LDS kernel (bf16, D a multiple of 64 up to 512; e4m3, D =
+  // 64, 128 or 256) folds the
   // scale into one FMA before exp2 and takes row maxima of the unscaled
   // scores, which needs scale > 0.  Every other D <= 256 case runs on the
   // generic tiled kernel and every other D > 256 case on the split-D kernels;

@@ -1,4 +1,4 @@
-// attn_dma.h -- direct-to-LDS K/V tile streaming shared by the bf16 kernels
+// attn_dma.h -- direct-to-LDS K/V tile streaming shared by the kernels
 // on gfx950: buffer descriptors in scalar registers, XOR swizzles matched to
 // the 64-bank LDS, per-lane load offsets and the loads themselves.
 #pragma once
@@ -23,6 +23,18 @@ template <int D>
 __device__ __forceinline__ int k_swz(int row) { return row & (D % 128 == 0 ? 15 : 7); }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) * (D % 128 == 0 ? 4 : 2); }
+
+// Swizzle of rows that are RP bytes long (RP a power of two times 16) read
+// as K fragments, rows 0..15 of a 16-lane phase at one logical chunk: the
+// RP/16 chunks of a row cover 16/(RP/16) rows' worth of one bank window, so
+// the XOR key steps once every 16/(RP/16) rows.  Used for e4m3 K rows (D
+// bytes each).
+template <int RP>
+__device__ __forceinline__ int k8_swz(int row) {
+  constexpr int NCH = RP / 16;
+  static_assert(NCH >= 4 && (NCH & (NCH - 1)) == 0, "row pitch");
+  return NCH >= 16 ? (row & 15) : ((row / (16 / NCH)) & (NCH - 1));
+}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -53,31 +65,40 @@ __device__ __forceinline__ i32x4 rsrc_at(i32x4 r, uint32_t off) {
   return t;
 }
 
-// Per-lane byte offsets (within one tile) of the direct-to-LDS loads of a K
-// (IS_V = false) or V tile.  Wave `wave` fills DMA_WAVE consecutive 1 KiB
-// blocks of the LDS tile; lane l writes bytes [16 l, 16 l + 16) of a block,
-// so the global chunk it fetches is the one the swizzle places there.
-template <typename C, bool IS_V>
-__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[C::DMA_WAVE], int wave, int lane) {
+// Per-lane byte offsets (within one tile of RP-byte rows) of N direct-to-LDS
+// loads.  Wave `wave` fills N consecutive 1 KiB blocks of the LDS tile; lane
+// l writes bytes [16 l, 16 l + 16) of a block, so the global chunk it
+// fetches is the one that swizzle `swz` (row -> XOR key) places there.
+template <int N, int RP, typename Swz>
+__device__ __forceinline__ void dma_offsets_rows(uint32_t (&voff)[N], int wave, int lane, Swz swz) {
 #pragma unroll
-  for (int j = 0; j < C::DMA_WAVE; ++j) {
-    const int o = (wave * C::DMA_WAVE + j) * 1024 + lane * 16;
-    const int row = o / C::RP;
-    const int pc = (o % C::RP) >> 4;
-    const int gc = pc ^ (IS_V ? v_swz<C::D>(row) : k_swz<C::D>(row));
-    voff[j] = (uint32_t)(row * C::RP + (gc << 4));
+  for (int j = 0; j < N; ++j) {
+    const int o = (wave * N + j) * 1024 + lane * 16;
+    const int row = o / RP;
+    const int pc = (o % RP) >> 4;
+    const int gc = pc ^ swz(row);
+    voff[j] = (uint32_t)(row * RP + (gc << 4));
   }
 }
 
-// Issue the direct-to-LDS loads of one tile (descriptor `rsrc`, positioned at
-// the tile) into LDS byte address `lds_tile`.  M0 holds each 1 KiB block's LDS
-// address.  Offsets at or past num_records read as zero.
-template <typename C>
-__device__ __forceinline__ void dma_tile(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[C::DMA_WAVE],
-                                         int wave) {
+// The same for a bf16 K (IS_V = false) or V tile of config C (row pitch
+// C::RP, C::DMA_WAVE loads per wave).
+template <typename C, bool IS_V>
+__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[C::DMA_WAVE], int wave, int lane) {
+  dma_offsets_rows<C::DMA_WAVE, C::RP>(voff, wave, lane,
+                                       [](int row) { return IS_V ? v_swz<C::D>(row) : k_swz<C::D>(row); });
+}
+
+// Issue N direct-to-LDS loads of one tile (descriptor `rsrc`, positioned at
+// the tile) into LDS byte address `lds_tile`.  M0 holds each 1 KiB block's
+// LDS address.  Offsets at or past num_records read as zero.
+template <int N>
+__device__ __forceinline__ void dma_blocks(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[N], int wave) {
 #pragma unroll
-  for (int j = 0; j < C::DMA_WAVE; ++j) {
-    const uint32_t lds_addr = lds_tile + (uint32_t)((wave * C::DMA_WAVE + j) * 1024);
+  for (int j = 0; j < N; ++j) {
+    // uniform by construction; readfirstlane keeps it in a scalar register
+    // when the compiler has placed the slot arithmetic in vector registers
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((wave * N + j) * 1024));
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
@@ -86,6 +107,12 @@ __device__ __forceinline__ void dma_tile(i32x4 rsrc, uint32_t lds_tile, const ui
         : "v"(voff[j]), "s"(rsrc), "s"(lds_addr)
         : "memory", "m0");
   }
+}
+
+template <typename C>
+__device__ __forceinline__ void dma_tile(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[C::DMA_WAVE],
+                                         int wave) {
+  dma_blocks<C::DMA_WAVE>(rsrc, lds_tile, voff, wave);
 }
 
 __device__ __forceinline__ void wait_vmem_all() {

@@ -1,5 +1,6 @@
-// attn_fwd_pipe.hip -- bf16 attention forward for gfx950 with direct-to-LDS
-// K/V streaming (head dims 64 and 128, positive scale).
+// attn_fwd_pipe.hip -- attention forward for gfx950 with direct-to-LDS K/V
+// streaming: bf16 for head dims 64..512 and e4m3 (fp8) for 64, 128 and 256,
+// positive scale.
 //
 // Same algorithm as the generic tiled kernel (FlashAttention summary page,
 // method paragraph; blog post "FlashAttention v1/v2/v3/v4", section "El truco
@@ -28,6 +29,14 @@
 //  * Row sums add the fp32 probabilities before rounding: a sum of the
 //    bf16-rounded values would move the LSE of short (early causal) rows by
 //    up to ~2^-9 relative.
+//  * e4m3 inputs (ZYFA article, "Why FP8 attention is softmax-bound on
+//    MI355X": only the two products change precision): K tiles stream into
+//    LDS as codes and feed the fp8 matrix instruction (64-wide contraction)
+//    against Q codes held in registers.  V is staged through registers one
+//    tile ahead, widened exactly to bf16 and written to LDS in the bf16
+//    layout, so P V runs on the bf16 matrix instruction with P rounded to
+//    bf16 as in the bf16 kernel.  The Q and K descales fold into the exp2
+//    multiplier and the V descale into the final 1/l.
 //  * Lazy rescale (ZYFA article, "The details that make it
 //    production-grade"): the running max moves, and O and l are rescaled,
 //    only when a row's new max exceeds it by more than 8 (base-2 units).
@@ -46,8 +55,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
-template <int D_, int NW_, int NBUF_, int BC_>
+template <int E_, int D_, int NW_, int NBUF_, int BC_>
 struct PipeCfg {
+  static constexpr bool FP8 = E_ == ELT_FP8;    // e4m3 Q/K/V, otherwise bf16
   static constexpr int D = D_;
   static constexpr int NW = NW_;                // waves per work-group
   static constexpr int NBUF = NBUF_;            // K/V tiles resident (ring)
@@ -57,37 +67,46 @@ struct PipeCfg {
   static constexpr int NT = NW * 64;            // threads per work-group
   static constexpr int QW = QB * 32;            // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per work-group
-  static constexpr int RP = D_ * 2;             // LDS row pitch (bytes)
-  static constexpr int TILE = BC * RP;          // bytes of one K or V tile
-  static constexpr int DMA_TILE = TILE / 1024;  // wave-wide 16 B/lane loads per tile
-  static constexpr int DMA_WAVE = DMA_TILE / NW;
+  static constexpr int ES = FP8 ? 1 : 2;        // bytes per input element
+  static constexpr int RPK = D_ * ES;           // K row pitch (bytes, HBM and LDS)
+  static constexpr int RP = D_ * 2;             // V row pitch in LDS (bf16)
+  static constexpr int TILE_K = BC * RPK;       // bytes of one K tile in LDS
+  static constexpr int TILE = BC * RP;          // bytes of one V tile in LDS
+  static constexpr int DMA_K = TILE_K / 1024 / NW;       // direct-to-LDS loads per wave, K tile
+  static constexpr int DMA_WAVE = FP8 ? 1 : TILE / 1024 / NW;  // same, V tile (bf16 only)
+  static constexpr int VST = FP8 ? BC * D_ / (16 * NT) : 1;    // e4m3 V: 16-byte loads per thread
   static constexpr int NDB = D_ / 32;           // 32-row blocks of O^T
-  static constexpr int NQC = D_ / 16;           // 16-wide d chunks of the QK^T contraction
+  static constexpr int NQC = D_ / 16;           // 16-wide d chunks of the bf16 QK^T contraction
+  static constexpr int NQ8 = D_ / 64;           // 64-wide d chunks of the e4m3 QK^T contraction
   static constexpr int NKB = BC / 32;           // 32-key blocks of S^T per tile
-  static constexpr int LDS = 2 * NBUF * TILE;   // K ring, V ring
+  static constexpr int LDS = NBUF * (TILE_K + TILE);  // K ring, V ring
   static constexpr int SW = (D_ % 128 == 0) ? 16 : 8;  // swizzle width (16-byte chunks)
   static constexpr int LK = NQC < 8 ? NQC : 8;  // K fragments in flight (large D)
   static constexpr int LV = NDB < 4 ? NDB : 4;  // V fragments in flight (large D)
   // s_waitcnt immediate for vmcnt(n): the loads of the NBUF-2 tiles issued
   // after a given tile may stay in flight (expcnt, lgkmcnt at their maxima)
-  static constexpr int LATER = (NBUF - 2) * 2 * DMA_WAVE;
+  static constexpr int LATER = (NBUF - 2) * (DMA_K + DMA_WAVE);
   static constexpr int WAIT_LATER = 0x0F70 | (LATER & 15) | ((LATER >> 4) << 14);
   static_assert(NBUF >= 2 && LATER < 64, "ring depth");
+  static_assert(!FP8 || NBUF == 2, "the e4m3 V staging assumes two buffers");
   static_assert(D_ % 64 == 0, "D must be a multiple of 64");
   static_assert(BC % 32 == 0, "BC must be a multiple of 32");
-  static_assert(DMA_TILE % NW == 0, "tile must split evenly over the waves");
+  static_assert(TILE_K % (1024 * NW) == 0 && TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(!FP8 || (BC * D_) % (16 * NT) == 0, "e4m3 V tile must split evenly over the threads");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int NW, int NBUF, int BC>
+template <int E, int D, int NW, int NBUF, int BC>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_fwd_pipe_kernel(FwdParams p) {
-  using C = PipeCfg<D, NW, NBUF, BC>;
+  using C = PipeCfg<E, D, NW, NBUF, BC>;
+  constexpr bool FP8 = C::FP8;
   constexpr int QB = C::QB;
   // LDS: K ring (NBUF tiles) then V ring (NBUF tiles)
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   // LDS byte address of the buffer (the M0 operand of the loads)
   const uint32_t lds_base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  char* const ldsV = lds + NBUF * C::TILE_K;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,36 +127,101 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 
   const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
   const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
-  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab, (uint32_t)((int64_t)p.Nq * D * 2));
-  const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, kv_bytes);
-  const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, kv_bytes);
+  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * C::ES);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc((const char*)p.q + q_slab * C::ES, (uint32_t)((int64_t)p.Nq * D * C::ES));
+  const i32x4 rk = sgpr_rsrc((const char*)p.k + kv_slab * C::ES, kv_bytes);
+  const i32x4 rv = sgpr_rsrc((const char*)p.v + kv_slab * C::ES, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv8 = make_rsrc((const char*)p.v + kv_slab * C::ES, kv_bytes);
 
-  const float c = p.scale * kLog2e;  // > 0 (the launcher routes other scales elsewhere)
+  // exp(x) = exp2(x log2 e); e4m3 folds the Q and K descales in here and the
+  // V descale into 1/l.  Positive (the launcher routes other scales elsewhere).
+  float c = p.scale * kLog2e;
+  float out_scale = 1.0f;
+  if constexpr (FP8) {
+    c *= (p.dq ? p.dq[0] : 1.0f) * (p.dk ? p.dk[0] : 1.0f);
+    out_scale = p.dv ? p.dv[0] : 1.0f;
+  }
 
   // ---- key range ------------------------------------------------------------------
   int kv_end = p.Nkv;
   if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
-  // ---- prologue loads: tiles 0 .. NBUF-2 (LDS), Q (registers) --------------------
-  uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
-  dma_offsets<C, false>(dk, wave, lane);
-  dma_offsets<C, true>(dv, wave, lane);
-  auto issue_tile = [&](int t, int slot) {
-    const uint32_t toff = (uint32_t)(t * C::TILE);
-    dma_tile<C>(rsrc_at(rk, toff), lds_base + (uint32_t)(slot * C::TILE), dk, wave);
-    dma_tile<C>(rsrc_at(rv, toff), lds_base + (uint32_t)((NBUF + slot) * C::TILE), dv, wave);
+  // ---- K/V staging ------------------------------------------------------------------
+  // K (either type) and bf16 V: direct-to-LDS loads.  e4m3 V: thread t loads
+  // 16-byte runs (16 codes of one key) u = t + i NT of the tile, widens them
+  // to two bf16 chunks and stores those where the bf16 layout puts them.
+  uint32_t dk[C::DMA_K], dv[C::DMA_WAVE];
+  if constexpr (FP8)
+    dma_offsets_rows<C::DMA_K, C::RPK>(dk, wave, lane, [](int row) { return k8_swz<C::RPK>(row); });
+  else
+    dma_offsets<C, false>(dk, wave, lane);
+  if constexpr (!FP8) dma_offsets<C, true>(dv, wave, lane);
+  auto issue_k = [&](int t, int slot) {
+    dma_blocks<C::DMA_K>(rsrc_at(rk, (uint32_t)(t * C::TILE_K)), lds_base + (uint32_t)(slot * C::TILE_K), dk,
+                         wave);
   };
+  auto issue_tile = [&](int t, int slot) {
+    issue_k(t, slot);
+    dma_tile<C>(rsrc_at(rv, (uint32_t)(t * C::TILE)), lds_base + (uint32_t)(NBUF * C::TILE_K + slot * C::TILE),
+                dv, wave);
+  };
+  constexpr int V8_CH = D / 16;  // 16-byte code runs per key row
+  u32x4 vst[C::VST];
+  auto v8_load = [&](int t) {
 #pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < n_kt) issue_tile(t, t);
-  u32x4 qf[QB][C::NQC];
+    for (int i = 0; i < C::VST; ++i) {
+      const int u = tid + i * C::NT;
+      vst[i] = buf_load16(rv8, (uint32_t)((t * C::BC + u / V8_CH) * D + (u % V8_CH) * 16));
+    }
+  };
+  auto v8_store = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < C::VST; ++i) {
+      const int u = tid + i * C::NT;
+      const int row = u / V8_CH, ch = u % V8_CH;
+      const u32x2 w0 = e4m3x4_to_bf16x4(vst[i].x), w1 = e4m3x4_to_bf16x4(vst[i].y);
+      const u32x2 w2 = e4m3x4_to_bf16x4(vst[i].z), w3 = e4m3x4_to_bf16x4(vst[i].w);
+      char* const vrow = ldsV + slot * C::TILE + row * C::RP;
+      lds_store16(vrow, (uint32_t)(((2 * ch) ^ v_swz<D>(row)) << 4), u32x4{w0.x, w0.y, w1.x, w1.y});
+      lds_store16(vrow, (uint32_t)(((2 * ch + 1) ^ v_swz<D>(row)) << 4), u32x4{w2.x, w2.y, w3.x, w3.y});
+    }
+  };
+
+  // ---- prologue loads: tiles 0 .. NBUF-2 (LDS), Q (registers) --------------------
+  if constexpr (FP8) {
+    // K tile 0 to LDS, V tile 0 widened into its slot, V tile 1 to registers
+    if (n_kt > 0) {
+      v8_load(0);
+      issue_k(0, 0);
+      v8_store(0);
+      if (n_kt > 1) v8_load(1);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < n_kt) issue_tile(t, t);
+  }
+  // Q fragments (B operand of S^T = K Q^T).  bf16: 16 d per instruction,
+  // lane half h holds d = 16cc + 8h .. +7.  e4m3: 64 d per instruction, lane
+  // half h holds d = 64cc + 32h .. +31.
+  u32x4 qf[QB][FP8 ? 1 : C::NQC];
+  i32x8 q8[QB][FP8 ? C::NQ8 : 1];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const uint32_t row_off = (uint32_t)(q0w + qb * 32 + l32) * (uint32_t)(D * 2);
+    const uint32_t row_off = (uint32_t)(q0w + qb * 32 + l32) * (uint32_t)C::RPK;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int cc = 0; cc < C::NQC; ++cc) qf[qb][cc] = buf_load16(rq, row_off + (uint32_t)(cc * 32 + h * 16));
+      for (int cc = 0; cc < C::NQ8; ++cc) {
+        const u32x4 lo = buf_load16(rq, row_off + (uint32_t)(cc * 64 + h * 32));
+        const u32x4 hi = buf_load16(rq, row_off + (uint32_t)(cc * 64 + h * 32 + 16));
+        q8[qb][cc] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < C::NQC; ++cc) qf[qb][cc] = buf_load16(rq, row_off + (uint32_t)(cc * 32 + h * 16));
+    }
   }
 
   f32x16 acc[QB][C::NDB];
@@ -162,6 +246,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 #pragma unroll
   for (int i = 0; i < KG; ++i) kbase[i] = (uint32_t)(l32 * C::RP + (((2 * i + h) ^ k_swz<D>(l32)) << 4));
   auto koff = [&](int cc) { return kbase[cc % KG] + (uint32_t)((cc / KG) * C::SW * 16); };
+  // e4m3 K fragment cc: row l32 (+32 kb), code chunks 4cc + 2h and 4cc + 2h + 1
+  uint32_t k8base[FP8 ? 2 * C::NQ8 : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 2 * C::NQ8; ++i)
+      k8base[i] = (uint32_t)(l32 * C::RPK + (((4 * (i >> 1) + 2 * h + (i & 1)) ^ k8_swz<C::RPK>(l32)) << 4));
+  }
   // V fragment (A operand of O^T += V^T P^T) via the transposing read: lane r
   // of each 16-lane group addresses row kbase + r/4, columns dbase + 4(r%4)..+3
   const int g16 = lane >> 4, r16 = lane & 15;
@@ -185,24 +276,63 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   for (int kt = 0; kt < n_kt; ++kt) {
     // Tile kt is resident once at most the loads of the NBUF-2 later tiles
     // are outstanding (loads complete in order); the barrier makes every
-    // wave's loads visible and frees the slot of tile kt-1 for reloading.
+    // wave's loads and LDS stores visible and frees the slot of tile kt-1.
     if (kt + NBUF - 2 < n_kt)
       __builtin_amdgcn_s_waitcnt(C::WAIT_LATER);
     else
       wait_vmem_all();
     __syncthreads();
-    if (kt + NBUF - 1 < n_kt) issue_tile(kt + NBUF - 1, slot == 0 ? NBUF - 1 : slot - 1);
-    const char* const kb_cur = lds + slot * C::TILE;
-    const char* const vb_cur = lds + (NBUF + slot) * C::TILE;
+    const int nslot = slot == 0 ? NBUF - 1 : slot - 1;  // slot of tile kt-1, free now
+    if constexpr (FP8) {
+      // V tile kt+1 (in registers since the last iteration) into its slot,
+      // V tile kt+2 into the registers, then K tile kt+1.  The K loads go
+      // last so that the wait the compiler places before the widening (it
+      // does not see them) never covers them.
+      if (kt + 1 < n_kt) {
+        v8_store(nslot);
+        if (kt + 2 < n_kt) v8_load(kt + 2);
+        issue_k(kt + 1, nslot);
+      }
+    } else {
+      if (kt + NBUF - 1 < n_kt) issue_tile(kt + NBUF - 1, nslot);
+    }
+    const char* const kb_cur = lds + slot * C::TILE_K;
+    const char* const vb_cur = ldsV + slot * C::TILE;
     slot = slot == NBUF - 1 ? 0 : slot + 1;
 
-    // ---- S^T = K Q^T ------------------------------------------------------------
+  // ---- S^T = K Q^T ------------------------------------------------------------
     f32x16 s[QB][C::NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) s[qb][kb] = f32x16{};
-    if constexpr (!C::LARGE) {
+    if constexpr (FP8) {
+      // e4m3: K fragments of one 32-key block (D/64 x 32 bytes per lane) are
+      // read before its MFMAs, the next block's while they run
+      auto kfrag8 = [&](int kb, int cc) {
+        const uint32_t kbo = (uint32_t)(kb * 32 * C::RPK);
+        const u32x4 lo = lds_load16(kb_cur, k8base[2 * cc] + kbo);
+        const u32x4 hi = lds_load16(kb_cur, k8base[2 * cc + 1] + kbo);
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      i32x8 kfa[C::NQ8], kfb[C::NQ8];
+#pragma unroll
+      for (int cc = 0; cc < C::NQ8; ++cc) kfa[cc] = kfrag8(0, cc);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        i32x8(&cur)[C::NQ8] = (kb & 1) ? kfb : kfa;
+        i32x8(&nxt)[C::NQ8] = (kb & 1) ? kfa : kfb;
+        if (kb + 1 < C::NKB) {
+#pragma unroll
+          for (int cc = 0; cc < C::NQ8; ++cc) nxt[cc] = kfrag8(kb + 1, cc);
+        }
+#pragma unroll
+        for (int cc = 0; cc < C::NQ8; ++cc) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_fp8(cur[cc], q8[qb][cc], s[qb][kb]);
+        }
+      }
+    } else if constexpr (!C::LARGE) {
       // K fragments of a whole 32-key block are read before its MFMAs, and the
       // next block's reads are issued before the current block's MFMAs, so LDS
       // latency overlaps the matrix work instead of stalling each instruction.
@@ -349,7 +479,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + xor32(l_run[qb]);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? out_scale / l_tot : 0.0f;
     const int qrow = q0w + qb * 32 + l32;
     if (qrow < p.Nq) {
       const int64_t orow = q_slab + (int64_t)qrow * D;
@@ -371,34 +501,43 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   }
 }
 
-template <int D, int NW, int NBUF, int BC>
+template <int E, int D, int NW, int NBUF, int BC>
 hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
-  using C = PipeCfg<D, NW, NBUF, BC>;
+  using C = PipeCfg<E, D, NW, NBUF, BC>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, NW, NBUF, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<E, D, NW, NBUF, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 LaunchFn pipe_launcher(int elt, int D) {
+  if (elt == ELT_FP8) {
+    switch (D) {
+      // e4m3 K rows of D bytes; V widened to bf16 in LDS
+      case 64: return &launch_pipe<ELT_FP8, 64, 4, 2, 64>;
+      case 128: return &launch_pipe<ELT_FP8, 128, 4, 2, 64>;
+      case 256: return &launch_pipe<ELT_FP8, 256, 4, 2, 32>;
+      default: return nullptr;
+    }
+  }
   if (elt != ELT_BF16) return nullptr;
   switch (D) {
     // two work-groups of 4 waves per CU, 64-key tiles, double-buffered
-    case 64: return &launch_pipe<64, 4, 2, 64>;
-    case 128: return &launch_pipe<128, 4, 2, 64>;
+    case 64: return &launch_pipe<ELT_BF16, 64, 4, 2, 64>;
+    case 128: return &launch_pipe<ELT_BF16, 128, 4, 2, 64>;
     // one work-group per CU: a wave holds Q[32, D] (D/8 VGPRs) and O (D/4
     // accumulators), 32-key tiles, double-buffered
-    case 192: return &launch_pipe<192, 4, 2, 32>;
-    case 256: return &launch_pipe<256, 4, 2, 32>;
-    case 320: return &launch_pipe<320, 4, 2, 32>;
-    case 384: return &launch_pipe<384, 4, 2, 32>;
-    case 448: return &launch_pipe<448, 4, 2, 32>;
-    case 512: return &launch_pipe<512, 4, 2, 32>;
+    case 192: return &launch_pipe<ELT_BF16, 192, 4, 2, 32>;
+    case 256: return &launch_pipe<ELT_BF16, 256, 4, 2, 32>;
+    case 320: return &launch_pipe<ELT_BF16, 320, 4, 2, 32>;
+    case 384: return &launch_pipe<ELT_BF16, 384, 4, 2, 32>;
+    case 448: return &launch_pipe<ELT_BF16, 448, 4, 2, 32>;
+    case 512: return &launch_pipe<ELT_BF16, 512, 4, 2, 32>;
     default: return nullptr;
   }
 }

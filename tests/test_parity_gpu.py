@@ -172,6 +172,15 @@ FP8_SMALL = [
     (1, 2, 2, 130, 200, 64, True),
     (1, 2, 2, 130, 200, 192, False),
     (1, 2, 1, 130, 200, 256, True),
+    # several key tiles, ragged tails, MQA
+    (1, 4, 1, 700, 1000, 128, False),
+    (1, 2, 2, 333, 517, 256, False),
+    (1, 2, 2, 200, 457, 64, False),
+    # more queries than keys, causal: the first rows see no key
+    (2, 2, 2, 260, 130, 128, True),
+    # exact tile multiples and a single element
+    (1, 2, 2, 128, 128, 128, True),
+    (1, 1, 1, 1, 1, 128, False),
 ]
 
 
@@ -180,6 +189,22 @@ FP8_SMALL = [
 def test_fp8_small_parity(case):
     B, Hq, Hkv, Nq, Nkv, D, causal = case
     full_parity(Workload("fp8small", B, Hq, Hkv, Nq, Nkv, D, causal, "fp8", seed=7, outlier_frac=0.01))
+
+
+def test_fp8_scale_variants():
+    # scale <= 0 takes the generic kernel, scale > 0 the direct-to-LDS one
+    for sc in (0.0, -0.3, 0.9):
+        w = Workload("fp8scale", 1, 2, 2, 150, 270, 128, True, "fp8", seed=11, outlier_frac=0.01)
+        note(f"fp8 scale={sc}")
+        inp = make_inputs(w)
+        q8, k8, v8, desc = inp
+        dev = torch.device("cuda:0")
+        dq, dk, dv = (torch.tensor([float(x)], dtype=torch.float32, device=dev) for x in desc)
+        o, lse = A.fwd_fp8(q8.to(dev), k8.to(dev), v8.to(dev), dq, dk, dv, causal=True, scale=sc)
+        torch.cuda.synchronize()
+        qq, kk, vv = oracle_inputs(w, inp)
+        Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref)
 
 
 def test_scale_variants_bf16():
