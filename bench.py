@@ -5,6 +5,13 @@ the workload, inputs resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+Without --warmup/--steps the counts are sized from a short probe so that the
+untimed warm-up lasts about 1.5 s and the timed loop about 1 s: under
+sustained load the GPU settles at a lower clock than in the first tens of
+milliseconds, and the timed steps should see the settled clock (the ZYFA
+article, "What the numbers establish, and where they overstate", makes the
+same point about sustained clocks).
+
 Throughput is matmul TFLOP/s: 4 * B * Hq * D * (visible query/key pairs) per
 step (the QK^T and PV products; softmax work is not counted).  The roofline
 object prices the same flops against the dense MFMA peak of the compute dtype,
@@ -34,11 +41,12 @@ DEFAULT_WORKLOAD = "prefill_causal_bf16"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 1 s of work)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: about 1.5 s of work)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0 = auto)")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0 = time budget)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -74,8 +82,9 @@ def make_step(w, dev_inp, out, lse):
     return lambda: A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)
 
 
-def cpu_baseline(w, host_inp, n_heads):
-    """Time the fp64 oracle on n_heads (batch, head) pairs of the workload."""
+def cpu_baseline(w, host_inp, n_heads, seconds):
+    """Time the fp64 oracle on (batch, head) slices of the workload: n_heads of
+    them, or (n_heads == 0) as many as fit in about `seconds` (at least one)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -84,7 +93,7 @@ def cpu_baseline(w, host_inp, n_heads):
         threads = 1
     G = w.Hq // w.Hkv
     rng = np.random.default_rng(1)
-    heads = [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads)]
+    order = [(int(b), int(h)) for b, h in zip(rng.integers(w.B, size=4 * w.B * w.Hq), rng.integers(w.Hq, size=4 * w.B * w.Hq))]
     if w.dtype == "fp8":
         q8, k8, v8, desc = host_inp
 
@@ -98,17 +107,22 @@ def cpu_baseline(w, host_inp, n_heads):
         get_q = lambda b, h: q[b, h].to(torch.float64).numpy()
         get_k = lambda b, h: k[b, h].to(torch.float64).numpy()
         get_v = lambda b, h: v[b, h].to(torch.float64).numpy()
+    done = 0
     t0 = time.perf_counter()
-    for b, hq in heads:
+    for b, hq in order:
         oracle.attention_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), w.scale, w.causal)
+        done += 1
+        dt = time.perf_counter() - t0
+        if (n_heads and done >= n_heads) or (not n_heads and dt >= seconds):
+            break
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * w.visible_pairs * len(heads)
+    flops = 4.0 * w.D * w.visible_pairs * done
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(heads)} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 numpy, "
+        "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name} (drawn at random, seed 1), fp64 numpy, "
                   f"S materialised per head; {dt:.1f} s wall, scaled by the same flop formula",
     }
 
@@ -123,7 +137,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     if args.copy_calibration_mib:
-        copy_calibration(args.copy_calibration_mib, args.steps)
+        copy_calibration(args.copy_calibration_mib, args.steps or 200)
         return
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -134,7 +148,20 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     step = make_step(w, dev_inp, out, lse)
 
-    for _ in range(args.warmup):
+    # size the warm-up and the timed loop from a short probe (its steps count
+    # as warm-up steps)
+    probe = 10 if args.warmup is None else min(10, args.warmup)
+    torch.cuda.synchronize()
+    t_probe = time.perf_counter()
+    for _ in range(probe):
+        step()
+    torch.cuda.synchronize()
+    est = max((time.perf_counter() - t_probe) / max(probe, 1), 1e-6)
+    if args.warmup is None:
+        args.warmup = int(min(20000, max(50, math.ceil(1.5 / est))))
+    if args.steps is None:
+        args.steps = int(min(5000, max(200, math.ceil(1.0 / est))))
+    for _ in range(max(0, args.warmup - probe)):
         step()
     torch.cuda.synchronize()
 
@@ -187,8 +214,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_heads or (6 if w.Nq * w.Nkv <= 4096 * 4096 else 2)
-        res["cpu_baseline"] = cpu_baseline(w, host_inp, n)
+        res["cpu_baseline"] = cpu_baseline(w, host_inp, args.cpu_heads, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -114,6 +114,11 @@ SMALL = [
     (1, 2, 2, 1, 500, 64, True, "bf16"),
     (1, 2, 2, 500, 1, 64, True, "bf16"),
     (1, 8, 1, 200, 190, 64, False, "bf16"),     # MQA
+    # several 256-row work-groups and 64-key tiles (causal offsets, tails)
+    (1, 2, 2, 700, 700, 128, True, "bf16"),
+    (1, 4, 2, 600, 1000, 128, True, "bf16"),
+    (2, 2, 1, 777, 777, 64, True, "bf16"),
+    (1, 2, 2, 513, 1500, 128, False, "bf16"),
     (1, 2, 2, 200, 211, 32, True, "bf16"),
     (1, 2, 2, 200, 211, 96, True, "bf16"),
     (1, 2, 2, 200, 211, 160, False, "bf16"),
