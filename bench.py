@@ -20,6 +20,7 @@ launch stream.  The cpu_baseline object times the fp64 oracle on a bounded
 sample of the same workload on the host cores.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -36,6 +37,36 @@ METRIC = "attention fwd TFLOPS on 1 MI355X and % of dense bf16/fp8 MFMA peak"
 # MI355X dense MFMA peaks (TFLOP/s): bf16 2.5 PF, fp8 5.0 PF, fp32 157.3 TF.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "prefill_causal_bf16"
+
+
+# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE per
+# dispatch, scaled by what the same counters read for a plain device copy of
+# known size: reads x2.00, writes x1.00), for the dominant kernel of a
+# workload.  Each entry is tied to a hash of the sources of that kernel;
+# when they have changed since the counters were taken, traffic is null.
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_io_aware_attn_amd", "csrc")
+MEASURED_TRAFFIC = {
+    # workload: (kernel sources, source hash, bytes read, bytes written)
+    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "98d4b9ed5d0be4d6",
+                            200380.6875 * 2 * 1024, 133308.125 * 1024),
+    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "98d4b9ed5d0be4d6",
+                    191872.125 * 2 * 1024, 99840.0 * 1024),
+    "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "47c44e5ab9c861a7",
+                          165828.9375 * 2 * 1024, 71214.0 * 1024),
+}
+
+
+def measured_traffic(name):
+    """HBM bytes per launch for the workload, or None if unmeasured or stale."""
+    entry = MEASURED_TRAFFIC.get(name)
+    if entry is None:
+        return None
+    files, digest, rd, wr = entry
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
+    return int(round(rd + wr)) if m.hexdigest()[:16] == digest else None
 
 
 def parse():
@@ -209,7 +240,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
         "cpu_baseline": None,
     }
