@@ -109,6 +109,45 @@ __device__ __forceinline__ void dma_blocks(i32x4 rsrc, uint32_t lds_tile, const 
   }
 }
 
+// Block j (a compile-time index once unrolled) of the N that wave `wave`
+// loads for one tile: lets a kernel spread a tile's loads between its MFMAs.
+// A wave stalls on a load until the address path accepts it; issued back to
+// back, a large tile's loads hold the wave for about the time the whole tile
+// takes to stream, while between MFMAs the matrix pipe keeps working meanwhile.
+template <int N>
+__device__ __forceinline__ void dma_block_at(i32x4 rsrc, uint32_t lds_tile, uint32_t voff, int wave, int j) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((wave * N + j) * 1024));
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void dma_block_one(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[N], int wave,
+                                              int j) {
+  dma_block_at<N>(rsrc, lds_tile, voff[j], wave, j);
+}
+
+// The offset dma_offsets computes for block j, computed on the spot for row
+// pitches that are a multiple of 1 KiB: then a block lies within one row, so
+// the row and its XOR key are uniform and only the chunk depends on the lane
+// (a few VALU instructions instead of one register per block held for the
+// whole kernel).
+template <typename C, bool IS_V>
+__device__ __forceinline__ uint32_t dma_offset_1k(int wave, int lane, int j) {
+  static_assert(C::RP % 1024 == 0, "row pitch must be a multiple of 1 KiB");
+  constexpr int BPR = C::RP / 1024;  // blocks per row
+  const int blk = wave * C::DMA_WAVE + j;
+  const int row = blk / BPR;
+  const int pc = (blk % BPR) * 64 + lane;
+  const int gc = pc ^ (IS_V ? v_swz<C::D>(row) : k_swz<C::D>(row));
+  return (uint32_t)(row * C::RP + (gc << 4));
+}
+
 template <typename C>
 __device__ __forceinline__ void dma_tile(i32x4 rsrc, uint32_t lds_tile, const uint32_t (&voff)[C::DMA_WAVE],
                                          int wave) {

@@ -60,11 +60,19 @@ struct SplitCfg {
   static constexpr int DMA_WAVE = TILE / 1024 / NW;
   static constexpr int NQC = DH / 16;              // QK^T k-steps per wave (16-col chunks 2cc + dh)
   static constexpr int NDB = DH / 32;              // 32-row blocks of O^T per wave (blocks 2db + dh)
+  // fragments in flight (K: one read each, V: two); smaller windows for the
+  // largest D, where Q alone takes D/8 VGPRs
+  static constexpr int LK = D_ >= 896 ? 4 : 8;
+  static constexpr int LV = D_ >= 896 ? 4 : 6;
+  static constexpr bool TWO_ACC = D_ < 960;        // second S accumulator (16 VGPRs)
+  static constexpr int KS = DMA_WAVE / 4;          // K(kt+1) blocks issued before the softmax
   static constexpr int XCH = NW * 64 * 16 * 4;     // partial-S exchange area
   static constexpr int LDS = 2 * TILE + XCH;
   static_assert(D_ % 64 == 0, "D must be a multiple of 64");
   static_assert((TILE / 1024) % NW == 0, "tile must split evenly over the waves");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  // one load block per two MFMAs in both the QK and the PV loop
+  static_assert(NQC == 2 * DMA_WAVE && 2 * NDB == 2 * DMA_WAVE, "load interleave");
 };
 
 template <int D>
@@ -111,6 +119,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
   dma_offsets<C, false>(dk, wave, lane);
   dma_offsets<C, true>(dv, wave, lane);
+  // offset of load block j inside the loop: recomputed when the row pitch
+  // allows it (D = 512, 1024), which frees the 2 DMA_WAVE offset registers
+  auto dma_off = [&](bool is_v, int j) -> uint32_t {
+    if constexpr (C::RP % 1024 == 0)
+      return is_v ? dma_offset_1k<C, true>(wave, lane, j) : dma_offset_1k<C, false>(wave, lane, j);
+    else
+      return is_v ? dv[j] : dk[j];
+  };
   if (n_kt > 0) {
     dma_tile<C>(rk, lk, dk, wave);
     dma_tile<C>(rv, lv, dv, wave);
@@ -161,13 +177,31 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
 
   for (int kt = 0; kt < n_kt; ++kt) {
     // ---- partial S^T over this wave's D/2 columns (chunks 2cc + dh) -------------
-    f32x16 s = f32x16{};
+    // K fragments through a rolling window of LK reads; two accumulators
+    // (even and odd chunks, where registers allow) so that consecutive MFMAs
+    // do not depend on each other.  V(kt) streams into its (free) buffer meanwhile, one block per
+    // two MFMAs (the first tile's V came with the prologue).
+    const i32x4 rv_t = rsrc_at(rv, (uint32_t)(kt * C::TILE));
+    f32x16 s;
+    {
+      auto kaddr = [&](int cc) { return kbase[cc % KG] + (uint32_t)((cc / KG) * KG * 64); };
+      u32x4 kf[C::LK];
 #pragma unroll
-    for (int cc = 0; cc < C::NQC; ++cc) {
-      const uint32_t off = kbase[cc % KG] + (uint32_t)((cc / KG) * KG * 64);
-      s = mfma_bf16(lds_load16(kbuf, off), qf[cc], s);
-      // bound how far the scheduler hoists fragment loads (registers)
-      if ((cc & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < C::LK; ++i) kf[i] = lds_load16(kbuf, kaddr(i));
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NQC; ++cc) {
+        const u32x4 cur = kf[cc % C::LK];
+        if (cc + C::LK < C::NQC) kf[cc % C::LK] = lds_load16(kbuf, kaddr(cc + C::LK));
+        __builtin_amdgcn_sched_barrier(0);
+        if ((cc & 1) && C::TWO_ACC)
+          s1 = mfma_bf16(cur, qf[cc], s1);
+        else
+          s0 = mfma_bf16(cur, qf[cc], s0);
+        if ((cc & 1) == 0 && kt > 0) dma_block_at<C::DMA_WAVE>(rv_t, lv, dma_off(true, cc >> 1), wave, cc >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = C::TWO_ACC ? s0 + s1 : s0;
     }
     // (float sub-vectors, not per-element bit casts: this compiler collapses
     // bit-cast elements of an MFMA result vector onto element 0)
@@ -177,7 +211,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     *reinterpret_cast<f32x4*>(xmine + 3072) = __builtin_shufflevector(s, s, 12, 13, 14, 15);
     wait_vmem_all();   // V(kt) resident
     __syncthreads();   // K buffer free, partials written, V(kt) visible
-    if (kt + 1 < n_kt) dma_tile<C>(rsrc_at(rk, (uint32_t)((kt + 1) * C::TILE)), lk, dk, wave);
+    // K(kt+1): the first KS blocks now (their issue overlaps the exchange
+    // read and the softmax), the rest between the PV MFMAs below
+    const bool k_next = kt + 1 < n_kt;
+    const i32x4 rk_n = rsrc_at(rk, (uint32_t)((kt + 1) * C::TILE));
+    if (k_next) {
+#pragma unroll
+      for (int j = 0; j < C::KS; ++j) dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, j), wave, j);
+    }
 
     // ---- S^T = own partial + peer partial --------------------------------------
     {
@@ -232,21 +273,39 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     l_run = ls;
 
     // ---- O^T[D/2 rows] += V^T P^T ------------------------------------------------------
-#pragma unroll
-    for (int s16 = 0; s16 < 2; ++s16) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
+    // V fragments (two transposing reads each) through a rolling window of
+    // LV; the remaining blocks of K(kt+1) go out evenly between the MFMAs.
+    {
+      auto vfrag = [&](int f) {
+        const int s16 = f / C::NDB, db = f % C::NDB;
         const uint32_t a0 = vbase[db % VG] + (uint32_t)(s16 * 16 * C::RP + (db / VG) * VG * 128);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vbuf + a0 + 8 * C::RP));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        acc[db] = mfma_bf16(u32x4{l2.x, l2.y, h2.x, h2.y}, pf[s16], acc[db]);
-        if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        return u32x4{l2.x, l2.y, h2.x, h2.y};
+      };
+      constexpr int NF = 2 * C::NDB;
+      u32x4 vf[C::LV];
+#pragma unroll
+      for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(i);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32x4 cur = vf[f % C::LV];
+        if (f + C::LV < NF) vf[f % C::LV] = vfrag(f + C::LV);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[f % C::NDB] = mfma_bf16(cur, pf[f / C::NDB], acc[f % C::NDB]);
+        if (k_next) {
+          // blocks KS + [ceil(f R / NF), ceil((f + 1) R / NF)), R = DMA_WAVE - KS
+          constexpr int R = C::DMA_WAVE - C::KS;
+#pragma unroll
+          for (int j = C::KS + (f * R + NF - 1) / NF; j < C::KS + ((f + 1) * R + NF - 1) / NF; ++j)
+            dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, j), wave, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     wait_vmem_all();   // K(kt+1) resident
     __syncthreads();   // V buffer free, exchange area read, K(kt+1) visible
-    if (kt + 1 < n_kt) dma_tile<C>(rsrc_at(rv, (uint32_t)((kt + 1) * C::TILE)), lv, dv, wave);
   }
 
   // ---- epilogue: this wave's 32-column blocks 2db + dh; LSE from the dh = 0 wave --
