@@ -293,9 +293,36 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         if (kt + 2 < n_kt) v8_load(kt + 2);
         issue_k(kt + 1, nslot);
       }
-    } else {
+    } else if constexpr (!C::LARGE) {
       if (kt + NBUF - 1 < n_kt) issue_tile(kt + NBUF - 1, nslot);
     }
+    // large D: the loads of tile kt+NBUF-1 go out between this tile's MFMAs
+    // (K blocks between the QK MFMAs, V blocks between the PV MFMAs): issued
+    // back to back here, they would hold the wave for about the time the
+    // tile takes to stream, with no other wave on its SIMD to fill the gap
+    const bool dma_next = C::LARGE && !FP8 && kt + NBUF - 1 < n_kt;
+    const i32x4 rk_n = rsrc_at(rk, (uint32_t)((kt + NBUF - 1) * C::TILE_K));
+    const i32x4 rv_n = rsrc_at(rv, (uint32_t)((kt + NBUF - 1) * C::TILE));
+    const uint32_t lk_n = lds_base + (uint32_t)(nslot * C::TILE_K);
+    const uint32_t lv_n = lds_base + (uint32_t)(NBUF * C::TILE_K + nslot * C::TILE);
+    // blocks [ceil(m N / M), ceil((m + 1) N / M)) of N after MFMA m of M
+    auto dma_between = [&](bool is_v, int m, int M) {
+      if constexpr (C::LARGE && !FP8) {
+        if (!dma_next) return;
+        constexpr int N = C::DMA_WAVE;
+#pragma unroll
+        for (int j = (m * N + M - 1) / M; j < ((m + 1) * N + M - 1) / M; ++j) {
+          // offsets recomputed where the row pitch allows it (frees the
+          // offset registers, which D = 512 needs)
+          uint32_t off;
+          if constexpr (C::RP % 1024 == 0)
+            off = is_v ? dma_offset_1k<C, true>(wave, lane, j) : dma_offset_1k<C, false>(wave, lane, j);
+          else
+            off = is_v ? dv[j] : dk[j];
+          dma_block_at<C::DMA_WAVE>(is_v ? rv_n : rk_n, is_v ? lv_n : lk_n, off, wave, j);
+        }
+      }
+    };
     const char* const kb_cur = lds + slot * C::TILE_K;
     const char* const vb_cur = ldsV + slot * C::TILE;
     slot = slot == NBUF - 1 ? 0 : slot + 1;
@@ -354,20 +381,22 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         }
       }
     } else {
-      // large D: a fixed number (LK) of K fragments in flight
+      // large D: a rolling window of LK K fragments over the whole tile
+      // (fragment f = (kb, cc)); the fences keep each read LK MFMAs ahead
+      constexpr int NF = C::NKB * C::NQC;
+      auto kaddr = [&](int f) { return koff(f % C::NQC) + (uint32_t)((f / C::NQC) * 32 * C::RP); };
+      u32x4 kf[C::LK];
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        const uint32_t kbo = (uint32_t)(kb * 32 * C::RP);
-        u32x4 kf[C::LK];
+      for (int i = 0; i < C::LK; ++i) kf[i] = lds_load16(kb_cur, kaddr(i));
 #pragma unroll
-        for (int i = 0; i < C::LK; ++i) kf[i] = lds_load16(kb_cur, koff(i) + kbo);
+      for (int f = 0; f < NF; ++f) {
+        const u32x4 cur = kf[f % C::LK];
+        if (f + C::LK < NF) kf[f % C::LK] = lds_load16(kb_cur, kaddr(f + C::LK));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < C::NQC; ++cc) {
-          const u32x4 cur = kf[cc % C::LK];
-          if (cc + C::LK < C::NQC) kf[cc % C::LK] = lds_load16(kb_cur, koff(cc + C::LK) + kbo);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_bf16(cur, qf[qb][cc], s[qb][kb]);
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb][f / C::NQC] = mfma_bf16(cur, qf[qb][f % C::NQC], s[qb][f / C::NQC]);
+        dma_between(false, f, NF);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -457,19 +486,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         }
       }
     } else {
-      // large D: a fixed number (LV) of V fragments in flight
+      // large D: a rolling window of LV V fragments over the whole tile
+      // (fragment f = (s16, db))
+      constexpr int NF = 2 * C::NKB * C::NDB;
+      u32x4 vf[C::LV];
 #pragma unroll
-      for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
-        u32x4 vf[C::LV];
+      for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(i / C::NDB, i % C::NDB);
 #pragma unroll
-        for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(s16, i);
+      for (int f = 0; f < NF; ++f) {
+        const u32x4 cur = vf[f % C::LV];
+        if (f + C::LV < NF) vf[f % C::LV] = vfrag((f + C::LV) / C::NDB, (f + C::LV) % C::NDB);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const u32x4 cur = vf[db % C::LV];
-          if (db + C::LV < C::NDB) vf[db % C::LV] = vfrag(s16, db + C::LV);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_bf16(cur, pf[qb][s16], acc[qb][db]);
-        }
+        for (int qb = 0; qb < QB; ++qb) acc[qb][f % C::NDB] = mfma_bf16(cur, pf[qb][f / C::NDB], acc[qb][f % C::NDB]);
+        dma_between(true, f, NF);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 

@@ -4,7 +4,7 @@ cross-compiles without a GPU).
 Each kernel source is compiled to assembly with the library's own flags and
 every kernel in it is checked for properties the design relies on:
 
-* no scratch (register spills), apart from two known, bounded cases;
+* no scratch (register spills), apart from one known, bounded case;
 * no packed fp32 instructions (the build disables them);
 * M0 written only inside the inline assembly of the direct-to-LDS loads, so
   the value those loads depend on is never clobbered by compiler-generated
@@ -25,8 +25,8 @@ from exact_io_aware_attn_amd import build as B
 KERNEL_SOURCES = ("attn_fwd_pipe.hip", "attn_fwd_splitd.hip", "attn_fwd_tiled.hip")
 
 # kernels allowed a small spill: (source, kernel name fragment) -> max bytes
+# (D = 1024 split-D: Q takes 128 VGPRs and O all 256 accumulation registers)
 KNOWN_SCRATCH = {
-    ("attn_fwd_pipe.hip", "attn_fwd_pipe_kernelILi1ELi512E"): 16,
     ("attn_fwd_splitd.hip", "attn_fwd_splitd_kernelILi1024E"): 16,
 }
 
