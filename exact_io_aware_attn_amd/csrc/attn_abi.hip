@@ -64,7 +64,8 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   // generic tiled kernel and every other D > 256 case on the split-D kernels;
   // both scale before masking.
   attn::LaunchFn fn = nullptr;
-  if (D <= 512 && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
+  if (scale > 0.0f) fn = attn::wide_launcher(elt, (int)D);
+  if (!fn && D <= 512 && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
   if (!fn) fn = D <= 256 ? attn::tiled_launcher(elt, (int)D) : attn::splitd_launcher(elt, (int)D);
   if (!fn)
     return fail(ATTN_ERR_UNSUPPORTED, "no kernel for dtype=%d D=%lld (fp32: D%%32==0, D<=128; fp8: D%%64==0, "

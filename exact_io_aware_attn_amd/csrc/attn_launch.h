@@ -38,6 +38,10 @@ LaunchFn tiled_launcher(int elt, int D);
 // e4m3: D = 64, 128 or 256; scale > 0), or nullptr.
 LaunchFn pipe_launcher(int elt, int D);
 
+// Launcher for the software-pipelined wide-head kernel (bf16, D a multiple
+// of 64 in [192, 512], scale > 0), or nullptr.
+LaunchFn wide_launcher(int elt, int D);
+
 // Launcher for the split-D kernels (bf16, 256 < D <= 1024), or nullptr.
 LaunchFn splitd_launcher(int elt, int D);
 

@@ -119,6 +119,12 @@ SMALL = [
     (1, 4, 2, 600, 1000, 128, True, "bf16"),
     (2, 2, 1, 777, 777, 64, True, "bf16"),
     (1, 2, 2, 513, 1500, 128, False, "bf16"),
+    # wide head dims: one or two key tiles only, keyless causal rows, tails
+    (1, 2, 2, 64, 32, 320, False, "bf16"),
+    (1, 2, 2, 129, 33, 256, False, "bf16"),
+    (1, 2, 1, 333, 517, 384, True, "bf16"),
+    (2, 2, 2, 150, 77, 448, True, "bf16"),
+    (1, 3, 3, 257, 1000, 512, False, "bf16"),
     (1, 2, 2, 200, 211, 32, True, "bf16"),
     (1, 2, 2, 200, 211, 96, True, "bf16"),
     (1, 2, 2, 200, 211, 160, False, "bf16"),
