@@ -91,7 +91,30 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Exchange a value with the lane 32 positions away (the other half-wave).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine each lane's value with that of lane l ^ 32 (the other half of the
+// wave).  v_permlane32_swap exchanges the upper half of one register with the
+// lower half of another; applied to two copies of x it leaves x's lower half
+// in both halves of one result and its upper half in both halves of the
+// other, so one VALU instruction replaces an LDS permute and its wait.  (The
+// two results are copied to scalars before the bit casts: a bit cast of an
+// element of the returned vector read element 0 for both.)
+__device__ __forceinline__ void wave_halves(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  wave_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  wave_halves(x, a, b);
+  return a + b;
+}
 
 // Round two floats to bf16 (RNE) and pack them, first in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

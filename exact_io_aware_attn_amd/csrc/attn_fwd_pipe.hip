@@ -424,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
-      const float mrow = fmaxf(mx, xor32(mx)) * c;  // scaled (base-2) units
+      const float mrow = max_halves(mx) * c;  // scaled (base-2) units
       if (__builtin_amdgcn_ballot_w64(mrow > m_run[qb] + kTau) != 0) {
         // rows that have seen no visible key yet keep m = -inf; exp2 of
         // (-inf) - 0 is 0 there, never (-inf) - (-inf)
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   // ---- epilogue ---------------------------------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
+    const float l_tot = sum_halves(l_run[qb]);
     const float inv = l_tot > 0.0f ? out_scale / l_tot : 0.0f;
     const int qrow = q0w + qb * 32 + l32;
     if (qrow < p.Nq) {

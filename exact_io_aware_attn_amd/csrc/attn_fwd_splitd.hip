@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-    const float mrow = fmaxf(mx, xor32(mx));  // base-2 units
+    const float mrow = max_halves(mx);  // base-2 units
     if (__builtin_amdgcn_ballot_w64(mrow > m_run + kTau) != 0) {
       const float m_new = fmaxf(m_run, mrow);
       const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.0f : m_new));
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: this wave's 32-column blocks 2db + dh; LSE from the dh = 0 wave --
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < p.Nq) {
     const int64_t orow = q_slab + (int64_t)qrow * D + dh * 32;

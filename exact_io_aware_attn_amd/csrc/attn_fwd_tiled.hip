@@ -339,7 +339,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = exp2_fast(m_run - m_use);
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = O / l (x dv for fp8), LSE = ln2 * (m + log2 l) ------------
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? out_scale / l_tot : 0.0f;
   if (qrow < p.Nq) {
     const int64_t orow = q_slab + (int64_t)qrow * D;

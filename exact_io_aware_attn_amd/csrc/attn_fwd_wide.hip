@@ -9,8 +9,9 @@
 // K/V tiles streamed into LDS by direct-to-LDS buffer loads.
 //
 // At these head dims a wave holds Q in D/4 VGPRs and O in D/2 accumulation
-// registers, so each SIMD runs one wave and no other wave can fill the matrix
-// pipe while it computes exponentials.  The wave overlaps the two itself:
+// registers, so a SIMD runs one wave (two at D = 192) and no other wave can
+// fill the matrix pipe while it computes exponentials.  The wave overlaps the
+// two itself:
 //
 //  * Iteration t computes S_t = K_t Q^T, then the product P_{t-1} V_{t-1} of
 //    the PREVIOUS tile, and between those MFMAs the exponentials, packing and
@@ -26,6 +27,9 @@
 //    P_{t-1} V_{t-1} MFMAs (V_0 with K_0 before the loop).  Two slots per
 //    operand suffice: iteration t reads K_t and V_{t-1} and writes K_{t+1}
 //    and V_t.
+//  * A tile is 32 keys, or 64 (NKB = 2 blocks of 32) where four such tiles
+//    fit in LDS (D = 256, 320): twice the work per barrier and per max
+//    reduction, measured faster there.
 //  * The ZYFA article ("The three techniques, in plain terms") describes the
 //    same goal -- exponentials off the matrix pipe's critical path -- reached
 //    there with two waves per SIMD; with one wave per SIMD the overlap has to
@@ -56,19 +60,22 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float alpha) {
   return r;
 }
 
-template <int D_>
+template <int D_, int NKB_>
 struct WideCfg {
   static constexpr int D = D_;
+  static constexpr int NKB = NKB_;              // 32-key blocks per tile
   static constexpr int NW = 4;                  // waves per work-group, one per SIMD
   static constexpr int NT = NW * 64;
   static constexpr int BR = NW * 32;            // query rows per work-group
-  static constexpr int BC = 32;                 // keys per tile
+  static constexpr int BC = 32 * NKB_;          // keys per tile
   static constexpr int RP = D_ * 2;             // LDS row pitch (bytes)
   static constexpr int TILE = BC * RP;          // one K or V tile
   static constexpr int DMA_WAVE = TILE / 1024 / NW;
   static constexpr int NDB = D_ / 32;           // 32-row blocks of O^T
-  static constexpr int NQC = D_ / 16;           // 16-wide d chunks of QK^T (MFMAs per S tile)
-  static constexpr int NFV = 2 * NDB;           // MFMAs per P V tile
+  static constexpr int NQC = D_ / 16;           // 16-wide d chunks of QK^T (MFMAs per 32-key block of S)
+  static constexpr int NFQ = NKB_ * NQC;        // MFMAs per S tile
+  static constexpr int NFV = 2 * NKB_ * NDB;    // MFMAs per P V tile
+  static constexpr int NE = 16 * NKB_;          // scores per lane per tile
   static constexpr int SW = (D_ % 128 == 0) ? 16 : 8;
   static constexpr int LK = 8;                  // K fragments in flight
   static constexpr int LV = 4;                  // V fragments in flight (8 reads)
@@ -78,9 +85,9 @@ struct WideCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int D>
+template <int D, int NKB>
 __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
-  using C = WideCfg<D>;
+  using C = WideCfg<D, NKB>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   const uint32_t lds_base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
@@ -164,7 +171,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
   const int qrow = q0w + l32;
   const int klim = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
 
-  u32x4 pprev[2] = {u32x4{}, u32x4{}};  // P_{t-1} (bf16), the B operand of this iteration's P V
+  u32x4 pprev[2 * NKB];  // P_{t-1} (bf16), the B operand of this iteration's P V
+#pragma unroll
+  for (int g = 0; g < 2 * NKB; ++g) pprev[g] = u32x4{};
 
   // ---- one iteration; HAS_QK: tile t exists, HAS_PV: tile t-1 exists ----------
   auto step = [&](int t, auto has_qk, auto has_pv) {
@@ -176,22 +185,26 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
     const char* const vb_prev = ldsV + ((t - 1) & 1) * C::TILE;
 
     // ---- S_t^T = K_t Q^T, K_{t+1} streaming in between the MFMAs --------------
-    f32x16 s = f32x16{};
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     float mneg = 0.0f;
     if constexpr (QK) {
       const bool k_next = t + 1 < n_kt;
       const i32x4 rk_n = rsrc_at(rk, (uint32_t)((t + 1) * C::TILE));
+      // fragment f: key block f / NQC, d chunk f % NQC
+      auto kfrag = [&](int f) { return lds_load16(kb_cur, koff(f % C::NQC) + (uint32_t)((f / C::NQC) * 32 * C::RP)); };
       u32x4 kf[C::LK];
 #pragma unroll
-      for (int i = 0; i < C::LK; ++i) kf[i] = lds_load16(kb_cur, koff(i));
+      for (int i = 0; i < C::LK; ++i) kf[i] = kfrag(i);
 #pragma unroll
-      for (int f = 0; f < C::NQC; ++f) {
+      for (int f = 0; f < C::NFQ; ++f) {
         const u32x4 cur = kf[f % C::LK];
-        if (f + C::LK < C::NQC) kf[f % C::LK] = lds_load16(kb_cur, koff(f + C::LK));
+        if (f + C::LK < C::NFQ) kf[f % C::LK] = kfrag(f + C::LK);
         __builtin_amdgcn_sched_barrier(0);
-        s = mfma_bf16(cur, qf[f], s);
+        s[f / C::NQC] = mfma_bf16(cur, qf[f % C::NQC], s[f / C::NQC]);
         if (k_next) {
-          constexpr int N = C::DMA_WAVE, M = C::NQC;
+          constexpr int N = C::DMA_WAVE, M = C::NFQ;
 #pragma unroll
           for (int j = (f * N + M - 1) / M; j < ((f + 1) * N + M - 1) / M; ++j)
             dma_block_at<C::DMA_WAVE>(rk_n, k_slot(t + 1), dma_off(false, j), wave, j);
@@ -202,20 +215,22 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
       const int key0 = t * C::BC;
       if ((key0 + C::BC > p.Nkv) || (p.causal && key0 + C::BC - 1 > q0w + p.kv_off)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          s[r] = key <= klim ? s[r] : -INFINITY;
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            s[kb][r] = key <= klim ? s[kb][r] : -INFINITY;
+          }
       }
       // running max.  O' + P_{t-1} V_{t-1} is due to be scaled by alpha;
       // alpha O' + (alpha P_{t-1}) V_{t-1} is the same, so O is scaled now
       // (before its MFMAs) and P_{t-1} with it.  The max moves up by a whole
       // number of base-2 units, which makes alpha a power of two and the
       // scaling of the bf16 P_{t-1} exact.
-      float mx = fmaxf(s[0], s[1]);
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-      const float mrow = fmaxf(mx, xor32(mx)) * c;
+      for (int i = 2; i < C::NE; i += 2) mx = fmaxf(fmaxf(mx, s[i / 16][i % 16]), s[i / 16][i % 16 + 1]);
+      const float mrow = max_halves(mx) * c;
       if (__builtin_amdgcn_ballot_w64(mrow > m_run + kTau) != 0) {
         float m_new = m_run;
         if (mrow > m_run) m_new = m_run == -INFINITY ? mrow : m_run + __builtin_ceilf(mrow - m_run);
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) scale_acc(acc[db], alpha);
 #pragma unroll
-          for (int g = 0; g < 2; ++g) pprev[g] = scale_bf16x8(pprev[g], alpha);
+          for (int g = 0; g < 2 * NKB; ++g) pprev[g] = scale_bf16x8(pprev[g], alpha);
         }
         l_run *= alpha;
         m_run = m_new;
@@ -234,10 +249,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
     }
 
     // ---- O^T += V_{t-1}^T P_{t-1}^T, with P_t computed between the MFMAs ------
-    float e[16];
+    float e[C::NE];
     auto exps = [&](int lo, int hi) {
 #pragma unroll
-      for (int i = lo; i < hi; ++i) e[i] = exp2_fast(__builtin_fmaf(s[i], c, mneg));
+      for (int i = lo; i < hi; ++i) e[i] = exp2_fast(__builtin_fmaf(s[i / 16][i % 16], c, mneg));
     };
     if constexpr (PV) {
       const bool v_now = t < n_kt;  // V_t streams in meanwhile
@@ -259,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
         if (f + C::LV < C::NFV) vf[f % C::LV] = vfrag(f + C::LV);
         __builtin_amdgcn_sched_barrier(0);
         acc[f % C::NDB] = mfma_bf16(cur, pprev[f / C::NDB], acc[f % C::NDB]);
-        if constexpr (QK) exps((f * 16 + C::NFV - 1) / C::NFV, ((f + 1) * 16 + C::NFV - 1) / C::NFV);
+        if constexpr (QK) exps((f * C::NE + C::NFV - 1) / C::NFV, ((f + 1) * C::NE + C::NFV - 1) / C::NFV);
         if (v_now) {
           constexpr int N = C::DMA_WAVE, M = C::NFV;
 #pragma unroll
@@ -269,12 +284,12 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      if constexpr (QK) exps(0, 16);
+      if constexpr (QK) exps(0, C::NE);
     }
     if constexpr (QK) {
       float ls = l_run;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < 2 * NKB; ++g) {
         pprev[g].x = pack_bf16x2(e[8 * g + 0], e[8 * g + 1]);
         pprev[g].y = pack_bf16x2(e[8 * g + 2], e[8 * g + 3]);
         pprev[g].z = pack_bf16x2(e[8 * g + 4], e[8 * g + 5]);
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------------
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < p.Nq) {
     const int64_t orow = q_slab + (int64_t)qrow * D;
@@ -315,15 +330,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
   }
 }
 
-template <int D>
+template <int D, int NKB>
 hipError_t launch_wide(const FwdParams& p0, hipStream_t stream) {
-  using C = WideCfg<D>;
+  using C = WideCfg<D, NKB>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_wide_kernel<D>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_wide_kernel<D, NKB>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -332,12 +347,13 @@ hipError_t launch_wide(const FwdParams& p0, hipStream_t stream) {
 LaunchFn wide_launcher(int elt, int D) {
   if (elt != ELT_BF16) return nullptr;
   switch (D) {
-    case 192: return &launch_wide<192>;
-    case 256: return &launch_wide<256>;
-    case 320: return &launch_wide<320>;
-    case 384: return &launch_wide<384>;
-    case 448: return &launch_wide<448>;
-    case 512: return &launch_wide<512>;
+    // 64-key tiles where two K and two V tiles fit in LDS and pay off
+    case 192: return &launch_wide<192, 1>;
+    case 256: return &launch_wide<256, 2>;
+    case 320: return &launch_wide<320, 2>;
+    case 384: return &launch_wide<384, 1>;
+    case 448: return &launch_wide<448, 1>;
+    case 512: return &launch_wide<512, 1>;
     default: return nullptr;
   }
 }

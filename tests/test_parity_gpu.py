@@ -125,6 +125,12 @@ SMALL = [
     (1, 2, 1, 333, 517, 384, True, "bf16"),
     (2, 2, 2, 150, 77, 448, True, "bf16"),
     (1, 3, 3, 257, 1000, 512, False, "bf16"),
+    # 64-key tiles of the wide kernel (D = 256, 320): several tiles, a ragged
+    # last tile, causal rows ending inside a tile's second 32-key block
+    (1, 2, 1, 300, 333, 256, True, "bf16"),
+    (2, 2, 1, 130, 97, 256, False, "bf16"),
+    (1, 2, 2, 257, 200, 320, True, "bf16"),
+    (1, 2, 2, 130, 450, 320, False, "bf16"),
     (1, 2, 2, 200, 211, 32, True, "bf16"),
     (1, 2, 2, 200, 211, 96, True, "bf16"),
     (1, 2, 2, 200, 211, 160, False, "bf16"),
