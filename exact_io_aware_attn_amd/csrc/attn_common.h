@@ -14,6 +14,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace attn {
@@ -114,6 +115,27 @@ __device__ __forceinline__ float sum_halves(float x) {
   float a, b;
   wave_halves(x, a, b);
   return a + b;
+}
+
+// An empty volatile use of an MFMA result at this point of the program.  The
+// optimiser otherwise sinks MFMAs (pure operations) towards their first use,
+// past the branches and barriers that follow them, and the matrix work meant
+// to overlap the code in between ends up after it.  The operand is an
+// accumulation register: a VGPR operand would copy the result out after
+// every MFMA and wait for it.
+__device__ __forceinline__ void pin_acc(const f32x16& x) { asm volatile("" : : "a"(x)); }
+// The same for a packed bf16 fragment computed by vector instructions.
+__device__ __forceinline__ void pin_frag(const u32x4& x) { asm volatile("" : : "v"(x)); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, each call its own
+// instantiation: loop bodies whose pieces depend on the index (if
+// constexpr) stay small, and arrays indexed by it stay in registers.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Round two floats to bf16 (RNE) and pack them, first in the low half.

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
           s1 = mfma_bf16(cur, qf[cc], s1);
         else
           s0 = mfma_bf16(cur, qf[cc], s0);
-        if ((cc & 1) == 0 && kt > 0) dma_block_at<C::DMA_WAVE>(rv_t, lv, dma_off(true, cc >> 1), wave, cc >> 1);
+        if (cc < C::DMA_WAVE && kt > 0) dma_block_at<C::DMA_WAVE>(rv_t, lv, dma_off(true, cc), wave, cc);
         __builtin_amdgcn_sched_barrier(0);
       }
       s = C::TWO_ACC ? s0 + s1 : s0;
@@ -295,11 +295,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         acc[f % C::NDB] = mfma_bf16(cur, pf[f / C::NDB], acc[f % C::NDB]);
         if (k_next) {
-          // blocks KS + [ceil(f R / NF), ceil((f + 1) R / NF)), R = DMA_WAVE - KS
-          constexpr int R = C::DMA_WAVE - C::KS;
-#pragma unroll
-          for (int j = C::KS + (f * R + NF - 1) / NF; j < C::KS + ((f + 1) * R + NF - 1) / NF; ++j)
-            dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, j), wave, j);
+          // blocks KS .. DMA_WAVE - 1, one after each of the first MFMAs
+          if (C::KS + f < C::DMA_WAVE) dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, C::KS + f), wave, C::KS + f);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
