@@ -47,12 +47,14 @@ DEFAULT_WORKLOAD = "prefill_causal_bf16"
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_io_aware_attn_amd", "csrc")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "98d4b9ed5d0be4d6",
-                            200380.6875 * 2 * 1024, 133308.125 * 1024),
-    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "98d4b9ed5d0be4d6",
-                    191872.125 * 2 * 1024, 99840.0 * 1024),
-    "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "47c44e5ab9c861a7",
-                          165828.9375 * 2 * 1024, 71214.0 * 1024),
+    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "9ceeec5c18c3f0ce",
+                            200970.15625 * 2 * 1024, 133447.265625 * 1024),
+    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "9ceeec5c18c3f0ce",
+                    190615.9375 * 2 * 1024, 99840.0 * 1024),
+    "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "5dfeb16e5630fc09",
+                          164425.9375 * 2 * 1024, 70206.59375 * 1024),
+    "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "a05ba7101835e860",
+                         49834.0 * 2 * 1024, 37840.125 * 1024),
 }
 
 

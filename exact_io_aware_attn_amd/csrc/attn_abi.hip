@@ -57,15 +57,15 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   if (B * Hq * ((Nq + 31) / 32) >= lim)
     return fail(ATTN_ERR_UNSUPPORTED, "grid too large: B*Hq*ceil(Nq/32) must be < 2^31");
 
-  // The direct-to-LDS kernel (bf16, D a multiple of 64 up to 512; e4m3, D =
-  // 64, 128 or 256) folds the
-  // scale into one FMA before exp2 and takes row maxima of the unscaled
+  // The wide-head kernel (bf16, D a multiple of 64 in [192, 512]) and the
+  // direct-to-LDS kernel (bf16, D = 64 or 128; e4m3, D = 64, 128 or 256) fold
+  // the scale into one FMA before exp2 and take row maxima of the unscaled
   // scores, which needs scale > 0.  Every other D <= 256 case runs on the
   // generic tiled kernel and every other D > 256 case on the split-D kernels;
   // both scale before masking.
   attn::LaunchFn fn = nullptr;
   if (scale > 0.0f) fn = attn::wide_launcher(elt, (int)D);
-  if (!fn && D <= 512 && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
+  if (!fn && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
   if (!fn) fn = D <= 256 ? attn::tiled_launcher(elt, (int)D) : attn::splitd_launcher(elt, (int)D);
   if (!fn)
     return fail(ATTN_ERR_UNSUPPORTED, "no kernel for dtype=%d D=%lld (fp32: D%%32==0, D<=128; fp8: D%%64==0, "

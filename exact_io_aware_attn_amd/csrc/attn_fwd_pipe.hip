@@ -1,6 +1,6 @@
 // attn_fwd_pipe.hip -- attention forward for gfx950 with direct-to-LDS K/V
-// streaming: bf16 for head dims 64..512 and e4m3 (fp8) for 64, 128 and 256,
-// positive scale.
+// streaming: bf16 for head dims 64 and 128 and e4m3 (fp8) for 64, 128 and
+// 256, positive scale.  (bf16 at larger head dims runs the wide-head kernel.)
 //
 // Same algorithm as the generic tiled kernel (FlashAttention summary page,
 // method paragraph; blog post "FlashAttention v1/v2/v3/v4", section "El truco
@@ -63,7 +63,7 @@ struct PipeCfg {
   static constexpr int NBUF = NBUF_;            // K/V tiles resident (ring)
   static constexpr int QB = 1;                  // 32-row query blocks per wave
   static constexpr int BC = BC_;                // keys per tile
-  static constexpr bool LARGE = D_ > 128;       // Q/O too large for 2 waves per SIMD
+  static constexpr bool LARGE = D_ > 128;       // Q/O too large for 2 waves per SIMD (e4m3 D = 256)
   static constexpr int NT = NW * 64;            // threads per work-group
   static constexpr int QW = QB * 32;            // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per work-group
@@ -94,6 +94,7 @@ struct PipeCfg {
   static_assert(TILE_K % (1024 * NW) == 0 && TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
   static_assert(!FP8 || (BC * D_) % (16 * NT) == 0, "e4m3 V tile must split evenly over the threads");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(!LARGE || FP8, "bf16 beyond D = 128 runs the wide-head kernel");
 };
 
 template <int E, int D, int NW, int NBUF, int BC>
@@ -296,33 +297,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
     } else if constexpr (!C::LARGE) {
       if (kt + NBUF - 1 < n_kt) issue_tile(kt + NBUF - 1, nslot);
     }
-    // large D: the loads of tile kt+NBUF-1 go out between this tile's MFMAs
-    // (K blocks between the QK MFMAs, V blocks between the PV MFMAs): issued
-    // back to back here, they would hold the wave for about the time the
-    // tile takes to stream, with no other wave on its SIMD to fill the gap
-    const bool dma_next = C::LARGE && !FP8 && kt + NBUF - 1 < n_kt;
-    const i32x4 rk_n = rsrc_at(rk, (uint32_t)((kt + NBUF - 1) * C::TILE_K));
-    const i32x4 rv_n = rsrc_at(rv, (uint32_t)((kt + NBUF - 1) * C::TILE));
-    const uint32_t lk_n = lds_base + (uint32_t)(nslot * C::TILE_K);
-    const uint32_t lv_n = lds_base + (uint32_t)(NBUF * C::TILE_K + nslot * C::TILE);
-    // blocks [ceil(m N / M), ceil((m + 1) N / M)) of N after MFMA m of M
-    auto dma_between = [&](bool is_v, int m, int M) {
-      if constexpr (C::LARGE && !FP8) {
-        if (!dma_next) return;
-        constexpr int N = C::DMA_WAVE;
-#pragma unroll
-        for (int j = (m * N + M - 1) / M; j < ((m + 1) * N + M - 1) / M; ++j) {
-          // offsets recomputed where the row pitch allows it (frees the
-          // offset registers, which D = 512 needs)
-          uint32_t off;
-          if constexpr (C::RP % 1024 == 0)
-            off = is_v ? dma_offset_1k<C, true>(wave, lane, j) : dma_offset_1k<C, false>(wave, lane, j);
-          else
-            off = is_v ? dv[j] : dk[j];
-          dma_block_at<C::DMA_WAVE>(is_v ? rv_n : rk_n, is_v ? lv_n : lk_n, off, wave, j);
-        }
-      }
-    };
     const char* const kb_cur = lds + slot * C::TILE_K;
     const char* const vb_cur = ldsV + slot * C::TILE;
     slot = slot == NBUF - 1 ? 0 : slot + 1;
@@ -395,7 +369,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][f / C::NQC] = mfma_bf16(cur, qf[qb][f % C::NQC], s[qb][f / C::NQC]);
-        dma_between(false, f, NF);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -499,7 +472,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][f % C::NDB] = mfma_bf16(cur, pf[qb][f / C::NDB], acc[qb][f % C::NDB]);
-        dma_between(true, f, NF);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -561,14 +533,6 @@ LaunchFn pipe_launcher(int elt, int D) {
     // two work-groups of 4 waves per CU, 64-key tiles, double-buffered
     case 64: return &launch_pipe<ELT_BF16, 64, 4, 2, 64>;
     case 128: return &launch_pipe<ELT_BF16, 128, 4, 2, 64>;
-    // one work-group per CU: a wave holds Q[32, D] (D/8 VGPRs) and O (D/4
-    // accumulators), 32-key tiles, double-buffered
-    case 192: return &launch_pipe<ELT_BF16, 192, 4, 2, 32>;
-    case 256: return &launch_pipe<ELT_BF16, 256, 4, 2, 32>;
-    case 320: return &launch_pipe<ELT_BF16, 320, 4, 2, 32>;
-    case 384: return &launch_pipe<ELT_BF16, 384, 4, 2, 32>;
-    case 448: return &launch_pipe<ELT_BF16, 448, 4, 2, 32>;
-    case 512: return &launch_pipe<ELT_BF16, 512, 4, 2, 32>;
     default: return nullptr;
   }
 }

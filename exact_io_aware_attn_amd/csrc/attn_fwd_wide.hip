@@ -23,10 +23,11 @@
 //    stale max then moves up by a whole number of base-2 units, so alpha_t is
 //    a power of two and scaling P_{t-1} is exact.  l follows the usual
 //    recurrence, updated with P_t.
-//  * K_{t+1} streams into LDS between the S_t MFMAs and V_t between the
-//    P_{t-1} V_{t-1} MFMAs (V_0 with K_0 before the loop).  Two slots per
-//    operand suffice: iteration t reads K_t and V_{t-1} and writes K_{t+1}
-//    and V_t.
+//  * K_{t+1} streams into LDS during the S_t MFMAs and V_t during the
+//    P_{t-1} V_{t-1} MFMAs (V_0 with K_0 before the loop), one load block
+//    after each of the phase's first MFMAs so the tile has the rest of the
+//    phase to land.  Two slots per operand suffice: iteration t reads K_t
+//    and V_{t-1} and writes K_{t+1} and V_t.
 //  * A tile is 32 keys, or 64 (NKB = 2 blocks of 32) where four such tiles
 //    fit in LDS (D = 256, 320): twice the work per barrier and per max
 //    reduction, measured faster there.
@@ -83,6 +84,7 @@ struct WideCfg {
   static_assert(D_ % 64 == 0 && D_ >= 192 && D_ <= 512, "head dims 192..512");
   static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(DMA_WAVE <= NFQ && DMA_WAVE <= NFV, "one load block per MFMA at most");
 };
 
 template <int D, int NKB>
@@ -203,12 +205,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
         if (f + C::LK < C::NFQ) kf[f % C::LK] = kfrag(f + C::LK);
         __builtin_amdgcn_sched_barrier(0);
         s[f / C::NQC] = mfma_bf16(cur, qf[f % C::NQC], s[f / C::NQC]);
-        if (k_next) {
-          constexpr int N = C::DMA_WAVE, M = C::NFQ;
-#pragma unroll
-          for (int j = (f * N + M - 1) / M; j < ((f + 1) * N + M - 1) / M; ++j)
-            dma_block_at<C::DMA_WAVE>(rk_n, k_slot(t + 1), dma_off(false, j), wave, j);
-        }
+        // one load block after each of the first MFMAs: the tile lands well
+        // before the barrier that needs it
+        if (k_next && f < C::DMA_WAVE) dma_block_at<C::DMA_WAVE>(rk_n, k_slot(t + 1), dma_off(false, f), wave, f);
         __builtin_amdgcn_sched_barrier(0);
       }
       // mask (tiles crossing the diagonal or the key tail only)
@@ -275,12 +274,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         acc[f % C::NDB] = mfma_bf16(cur, pprev[f / C::NDB], acc[f % C::NDB]);
         if constexpr (QK) exps((f * C::NE + C::NFV - 1) / C::NFV, ((f + 1) * C::NE + C::NFV - 1) / C::NFV);
-        if (v_now) {
-          constexpr int N = C::DMA_WAVE, M = C::NFV;
-#pragma unroll
-          for (int j = (f * N + M - 1) / M; j < ((f + 1) * N + M - 1) / M; ++j)
-            dma_block_at<C::DMA_WAVE>(rv_t, v_slot(t), dma_off(true, j), wave, j);
-        }
+        if (v_now && f < C::DMA_WAVE) dma_block_at<C::DMA_WAVE>(rv_t, v_slot(t), dma_off(true, f), wave, f);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {

@@ -34,8 +34,8 @@ typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 // (attn::Elt) and head dim D, or nullptr if that pair is not instantiated.
 LaunchFn tiled_launcher(int elt, int D);
 
-// Launcher for the direct-to-LDS kernel (bf16: D a multiple of 64 up to 512;
-// e4m3: D = 64, 128 or 256; scale > 0), or nullptr.
+// Launcher for the direct-to-LDS kernel (bf16: D = 64 or 128; e4m3: D = 64,
+// 128 or 256; scale > 0), or nullptr.
 LaunchFn pipe_launcher(int elt, int D);
 
 // Launcher for the software-pipelined wide-head kernel (bf16, D a multiple
