@@ -13,6 +13,9 @@ online         -- the online-softmax recurrence over key blocks (running max m,
                   running sum l, rescaled output), used only to pin that the
                   blockwise algorithm reproduces the plain definition.
 e4m3           -- decoding of OCP FP8 E4M3FN codes to exact float64 values.
+keyrange       -- attention over one range of the keys (causal alignment of the
+                  whole problem) and the log-sum-exp merge of such partial
+                  results (split-KV, chunked prefill).
 
 Every function cites the passage of the source pages it follows, by page title
 and section.  No function here is "parity unpinned": each one is pinned by a
@@ -22,6 +25,7 @@ a library cross-check and a hand-worked example under ``tests/golden/``).
 from .exact import attention, attention_head, kv_head_of, visible_mask
 from .online import online_attention_head
 from .e4m3 import e4m3fn_decode, E4M3FN_MAX
+from .keyrange import attention_range, attention_range_head, key_range_mask, merge
 
 __all__ = [
     "attention",
@@ -31,4 +35,8 @@ __all__ = [
     "online_attention_head",
     "e4m3fn_decode",
     "E4M3FN_MAX",
+    "attention_range",
+    "attention_range_head",
+    "key_range_mask",
+    "merge",
 ]

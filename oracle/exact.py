@@ -84,7 +84,16 @@ def attention_head(q, k, v, scale, causal=False, rows=None):
     rows = np.asarray(rows, dtype=np.int64)
     qs = q[rows]
     S = (qs @ k.T) * np.float64(scale)                  # (R, Nkv), materialised
-    vis = visible_mask(Nq, Nkv, causal, rows)
+    return masked_softmax_pv(S, visible_mask(Nq, Nkv, causal, rows), v)
+
+
+def masked_softmax_pv(S, vis, v):
+    """Softmax of each row of S over the entries where ``vis`` is True, times
+    v; returns (O, LSE).  A row with no True entry gets O = 0, LSE = -inf.
+
+    The max-subtracted softmax of the blog post (section "El truco que hizo
+    posible todo: online softmax"), natural log for the LSE.
+    """
     S = np.where(vis, S, -np.inf)
     any_vis = vis.any(axis=1)
     m = np.where(any_vis, S.max(axis=1, initial=-np.inf), 0.0)

@@ -20,6 +20,7 @@ import torch
 
 import oracle
 import oracle.exact as oatt
+import oracle.keyrange as omerge
 from oracle import attention, attention_head, e4m3fn_decode, online_attention_head
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -250,10 +251,84 @@ def check_rows_subset():
     return bool(ok)
 
 
+def _brute_range(q, k, v, scale, causal, kv_begin, kv_end):
+    """Scalar loops over one (b, head), keys restricted to [kv_begin, kv_end)."""
+    Nq, D = q.shape
+    Nkv = k.shape[0]
+    O = [[0.0] * v.shape[1] for _ in range(Nq)]
+    L = [0.0] * Nq
+    for i in range(Nq):
+        vis = [j for j in range(kv_begin, kv_end) if (not causal) or j <= i + Nkv - Nq]
+        if not vis:
+            L[i] = -math.inf
+            continue
+        s = {j: scale * math.fsum(float(q[i, d]) * float(k[j, d]) for d in range(D)) for j in vis}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in vis}
+        tot = math.fsum(w.values())
+        for c in range(v.shape[1]):
+            O[i][c] = math.fsum(w[j] * float(v[j, c]) for j in vis) / tot
+        L[i] = mx + math.log(tot)
+    return np.array(O), np.array(L)
+
+
+def check_range_brute_force():
+    """Attention over a key range against scalar loops (absolute causal index)."""
+    ok = True
+    for seed, (Nq, Nkv, D, causal, kb, ke) in enumerate([(5, 9, 3, True, 2, 7), (6, 4, 4, True, 1, 3),
+                                                         (4, 8, 2, False, 3, 8), (7, 7, 3, True, 0, 4)]):
+        q, k, v = rng_arrays(300 + seed, (Nq, D), (Nkv, D), (Nkv, D))
+        O, L = omerge.attention_range_head(q, k, v, 0.45, causal, kb, ke)
+        Ob, Lb = _brute_range(q, k, v, 0.45, causal, kb, ke)
+        ok &= np.allclose(O, Ob, rtol=0, atol=1e-12)
+        fin = np.isfinite(Lb)
+        ok &= bool(np.array_equal(fin, np.isfinite(L)))
+        ok &= np.allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_range_partition_merges_to_whole():
+    """Any partition of the keys into ranges merges back to full attention."""
+    ok = True
+    cases = [(1, 4, 2, 12, 30, 8, True), (2, 2, 1, 20, 20, 4, False), (1, 3, 3, 25, 9, 5, True),
+             (1, 2, 2, 9, 40, 6, True)]
+    for seed, (B, Hq, Hkv, Nq, Nkv, D, causal) in enumerate(cases):
+        q, k, v = rng_arrays(400 + seed, (B, Hq, Nq, D), (B, Hkv, Nkv, D), (B, Hkv, Nkv, D))
+        O, L = attention(q, k, v, 0.6, causal)
+        rng = np.random.default_rng(500 + seed)
+        for n_parts in (1, 2, 3, 5):
+            cuts = np.sort(rng.choice(np.arange(1, Nkv), size=min(n_parts - 1, Nkv - 1), replace=False))
+            edges = [0, *cuts.tolist(), Nkv]
+            parts = [omerge.attention_range(q, k, v, 0.6, causal, a, b) for a, b in zip(edges[:-1], edges[1:])]
+            Om, Lm = omerge.merge([p[0] for p in parts], [p[1] for p in parts])
+            ok &= np.allclose(Om, O, rtol=0, atol=1e-12)
+            fin = np.isfinite(L)
+            ok &= bool(np.array_equal(fin, np.isfinite(Lm)))
+            ok &= np.allclose(Lm[fin], L[fin], rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_merge_edge_cases():
+    """One part is returned as is; an empty part (LSE = -inf) changes nothing;
+    rows empty in every part give O = 0, LSE = -inf."""
+    rng = np.random.default_rng(600)
+    O1 = rng.standard_normal((3, 5, 4))
+    L1 = rng.standard_normal((3, 5))
+    Om, Lm = omerge.merge(O1[None], L1[None])
+    ok = np.allclose(Om, O1, rtol=0, atol=1e-15) and np.allclose(Lm, L1, rtol=0, atol=1e-15)
+    empty_L = np.full((3, 5), -np.inf)
+    Om2, Lm2 = omerge.merge(np.stack([O1, np.zeros_like(O1)]), np.stack([L1, empty_L]))
+    ok &= np.allclose(Om2, O1, rtol=0, atol=1e-15) and np.allclose(Lm2, L1, rtol=0, atol=1e-15)
+    Om3, Lm3 = omerge.merge(np.zeros((2, 3, 5, 4)), np.stack([empty_L, empty_L]))
+    ok &= bool(np.all(Om3 == 0) and np.all(np.isneginf(Lm3)))
+    return bool(ok)
+
+
 ALL_CHECKS = [check_golden, check_brute_force, check_library_sdpa, check_rows_sum_to_one,
               check_identical_keys, check_one_hot, check_row_shift, check_causal_prefix,
               check_gqa_repeat, check_merge, check_permutations, check_no_visible_rows,
-              check_rows_subset]
+              check_rows_subset, check_range_brute_force, check_range_partition_merges_to_whole,
+              check_merge_edge_cases]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -345,21 +420,51 @@ def _mut_sqrt_scale(q, k, v, scale, causal=False, rows=None):
     return _real_head(q, k, v, math.sqrt(abs(scale)), causal, rows)
 
 
+_real_range_mask = omerge.key_range_mask
+_real_merge = omerge.merge
+
+
+def _mut_range_end_inclusive(Nq, Nkv, causal, kv_begin, kv_end, rows=None):
+    return _real_range_mask(Nq, Nkv, causal, kv_begin, kv_end + 1, rows)
+
+
+def _mut_range_relative_causal(Nq, Nkv, causal, kv_begin, kv_end, rows=None):
+    # causal alignment taken relative to the range instead of the whole problem
+    vis = oatt.visible_mask(Nq, kv_end - kv_begin, causal, rows)
+    out = np.zeros((vis.shape[0], Nkv), bool)
+    out[:, kv_begin:kv_end] = vis
+    return out
+
+
+def _mut_merge_mean(O_parts, LSE_parts):
+    _, L = _real_merge(O_parts, LSE_parts)
+    return np.asarray(O_parts, dtype=np.float64).mean(axis=0), L
+
+
+def _mut_merge_max_lse(O_parts, LSE_parts):
+    O, _ = _real_merge(O_parts, LSE_parts)
+    return O, np.asarray(LSE_parts, dtype=np.float64).max(axis=0)
+
+
 MUTATIONS = {
-    "gqa_modulo": ("kv_head_of", _mut_gqa),
-    "causal_top_left": ("visible_mask", _mut_topleft),
-    "causal_strict": ("visible_mask", _mut_strict),
-    "scale_dropped": ("attention_head", _mut_no_scale),
-    "lse_base2": ("attention_head", _mut_lse_log2),
-    "v_rows_misindexed": ("attention_head", _mut_v_reversed),
-    "scale_sqrt": ("attention_head", _mut_sqrt_scale),
+    "gqa_modulo": (oatt, "kv_head_of", _mut_gqa),
+    "causal_top_left": (oatt, "visible_mask", _mut_topleft),
+    "causal_strict": (oatt, "visible_mask", _mut_strict),
+    "scale_dropped": (oatt, "attention_head", _mut_no_scale),
+    "lse_base2": (oatt, "attention_head", _mut_lse_log2),
+    "v_rows_misindexed": (oatt, "attention_head", _mut_v_reversed),
+    "scale_sqrt": (oatt, "attention_head", _mut_sqrt_scale),
+    "range_end_inclusive": (omerge, "key_range_mask", _mut_range_end_inclusive),
+    "range_causal_relative": (omerge, "key_range_mask", _mut_range_relative_causal),
+    "merge_mean": (omerge, "merge", _mut_merge_mean),
+    "merge_lse_max": (omerge, "merge", _mut_merge_max_lse),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistakes_are_caught(name, monkeypatch):
-    attr, fn = MUTATIONS[name]
-    monkeypatch.setattr(oatt, attr, fn)
+    mod, attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, fn)
     # the checks call through the module so that the mutation is seen
     monkeypatch.setattr(oracle, "attention_head", oatt.attention_head, raising=False)
     me = sys.modules[__name__]
