@@ -18,7 +18,8 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/attn.h declares
-EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_last_error", "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
+            "attn_fwd_splitkv", "attn_status_string", "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -45,6 +46,16 @@ def lib():
     L.attn_fwd.restype = ci
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
     L.attn_fwd_fp8.restype = ci
+    L.attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, i64, i64,
+                                   vp, vp, vp, vp]
+    L.attn_fwd_partial.restype = ci
+    L.attn_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, i64, ci, vp]
+    L.attn_merge.restype = ci
+    L.attn_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    L.attn_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, vp, vp, vp,
+                                   i64, vp, ctypes.c_size_t, vp]
+    L.attn_fwd_splitkv.restype = ci
     L.attn_status_string.argtypes = [ci]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -147,3 +158,97 @@ def fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=Fals
                        lse.data_ptr() if lse is not None else None,
                        B, Hq, Hkv, Nq, Nkv, D, causal, scale, *ptrs, _stream_ptr(stream)))
     return out, lse
+
+
+def _dtype_code(q, k, v):
+    if q.dtype == torch.float32:
+        dt = ATTN_F32
+    elif q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dt = ATTN_FP8_E4M3
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    return dt
+
+
+def _descale_ptrs(dt, descales):
+    if descales is None:
+        return [None, None, None]
+    if dt != ATTN_FP8_E4M3:
+        raise ValueError("descales apply to float8_e4m3fn inputs only")
+    ptrs = []
+    for d in descales:
+        if d is None:
+            ptrs.append(None)
+            continue
+        if d.dtype != torch.float32 or not d.is_cuda or d.numel() < 1:
+            raise ValueError("descales must be float32 device tensors with one element")
+        ptrs.append(d.data_ptr())
+    return ptrs
+
+
+def fwd_partial(q, k, v, kv_begin, kv_end, causal=False, scale=None, descales=None, stream=None):
+    """Attention of q over the keys kv_begin <= j < kv_end of k/v (the whole
+    sequence's causal alignment).  ``descales``: (dq, dk, dv) one-element
+    float32 device tensors for e4m3 inputs, or None.  Returns float32
+    (o_part, lse_part)."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    dt = _dtype_code(q, k, v)
+    dptr = _descale_ptrs(dt, descales)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Hq, Nq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, int(kv_begin), int(kv_end),
+                                  *dptr, _stream_ptr(stream)))
+    return o, lse
+
+
+def merge(o_parts, lse_parts, out_dtype=torch.bfloat16, return_lse=True, stream=None):
+    """Merge float32 partial results (P, B, Hq, Nq, D) / (P, B, Hq, Nq) by LSE."""
+    if o_parts.dim() != 5 or lse_parts.dim() != 4 or tuple(o_parts.shape[:4]) != tuple(lse_parts.shape):
+        raise ValueError("o_parts must be (P, B, Hq, Nq, D) and lse_parts (P, B, Hq, Nq)")
+    for t in (o_parts, lse_parts):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("partial results must be contiguous float32 device tensors")
+    P, B, Hq, Nq, D = o_parts.shape
+    code = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}.get(out_dtype)
+    if code is None:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    o = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=o_parts.device) if return_lse else None
+    _check(lib().attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), P, o.data_ptr(),
+                            lse.data_ptr() if lse is not None else None, B, Hq, Nq, D, code, _stream_ptr(stream)))
+    return o, lse
+
+
+def splitkv_workspace_bytes(B, Hq, Nq, D, n_splits):
+    return int(lib().attn_splitkv_workspace_bytes(B, Hq, Nq, D, n_splits))
+
+
+def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, workspace=None, stream=None):
+    """``fwd`` (or ``fwd_fp8`` with ``descales``) computed as ``n_splits`` key
+    ranges in one launch plus a merge.
+
+    ``workspace``: optional uint8 device tensor of at least
+    ``splitkv_workspace_bytes`` bytes (allocated here by torch otherwise).
+    Returns (o, lse) like ``fwd``.
+    """
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    dt = _dtype_code(q, k, v)
+    dptr = _descale_ptrs(dt, descales)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = splitkv_workspace_bytes(B, Hq, Nq, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, Hq, Nq, D), dtype=torch.float32 if dt == ATTN_F32 else torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, *dptr, int(n_splits),
+                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+    return o, lse

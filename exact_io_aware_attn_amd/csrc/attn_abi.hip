@@ -23,9 +23,18 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Key ranges of one forward launch: n_splits ranges of split_len keys from
+// kv_begin (the last one ends at kv_end); outputs of split s at o + s *
+// o_split_stride, lse + s * lse_split_stride; o in float32 when o_f32.
+struct Ranges {
+  int64_t kv_begin, kv_end, split_len, n_splits;
+  bool o_f32;
+  int64_t o_split_stride, lse_split_stride;
+};
+
 int run_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
-                const float* dq, const float* dk, const float* dv, attn_stream_t stream) {
+                const float* dq, const float* dk, const float* dv, const Ranges* ranges, attn_stream_t stream) {
   g_last_error[0] = '\0';
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL device pointers");
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
@@ -46,7 +55,7 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
 
   const int elt = dtype == ATTN_F32 ? attn::ELT_F32 : dtype == ATTN_BF16 ? attn::ELT_BF16 : attn::ELT_FP8;
   const int64_t in_bytes = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
-  const int64_t out_bytes = dtype == ATTN_F32 ? 4 : 2;
+  const int64_t out_bytes = (dtype == ATTN_F32 || (ranges && ranges->o_f32)) ? 4 : 2;
   const int64_t lim = (int64_t)1 << 31;
   if (D > 1024 || D % 32 != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: D must be a multiple of 32 in [32, 1024]", (long long)D);
@@ -54,8 +63,9 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
     return fail(ATTN_ERR_UNSUPPORTED, "a (batch, head) slab of q, k, v or o reaches 2^31 bytes");
   if (B * Hq > (int64_t)INT32_MAX || Nq > INT32_MAX || Nkv > INT32_MAX)
     return fail(ATTN_ERR_UNSUPPORTED, "B*Hq and sequence lengths must fit in 31 bits");
-  if (B * Hq * ((Nq + 31) / 32) >= lim)
-    return fail(ATTN_ERR_UNSUPPORTED, "grid too large: B*Hq*ceil(Nq/32) must be < 2^31");
+  const int64_t n_splits = ranges ? ranges->n_splits : 1;
+  if (B * Hq * ((Nq + 31) / 32) * n_splits >= lim)
+    return fail(ATTN_ERR_UNSUPPORTED, "grid too large: splits*B*Hq*ceil(Nq/32) must be < 2^31");
 
   // The wide-head kernel (bf16, D a multiple of 64 in [192, 512]) and the
   // direct-to-LDS kernel (bf16, D = 64 or 128; e4m3, D = 64, 128 or 256) fold
@@ -89,6 +99,23 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  if (ranges) {
+    p.kv_begin = (int)ranges->kv_begin;
+    p.kv_end = (int)ranges->kv_end;
+    p.split_len = (int)ranges->split_len;
+    p.n_splits = (int)ranges->n_splits;
+    p.o_f32 = ranges->o_f32 ? 1 : 0;
+    p.o_split_stride = ranges->o_split_stride;
+    p.lse_split_stride = ranges->lse_split_stride;
+  } else {
+    p.kv_begin = 0;
+    p.kv_end = (int)Nkv;
+    p.split_len = (int)Nkv;
+    p.n_splits = 1;
+    p.o_f32 = dtype == ATTN_F32 ? 1 : 0;
+    p.o_split_stride = 0;
+    p.lse_split_stride = 0;
+  }
   hipError_t err = fn(p, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ATTN_OK;
@@ -102,14 +129,114 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
              attn_stream_t stream) {
   return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, nullptr, nullptr, nullptr,
-                     stream);
+                     nullptr, stream);
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                  int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale,
                  const float* descale_q, const float* descale_k, const float* descale_v, attn_stream_t stream) {
   return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_FP8_E4M3, descale_q, descale_k,
-                     descale_v, stream);
+                     descale_v, nullptr, stream);
+}
+
+int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,
+                     int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
+                     int64_t kv_begin, int64_t kv_end, const float* descale_q, const float* descale_k,
+                     const float* descale_v, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (!lse_part) return fail(ATTN_ERR_INVALID_ARG, "lse_part must be a non-NULL device pointer");
+  if (kv_begin < 0 || kv_begin > kv_end || kv_end > Nkv)
+    return fail(ATTN_ERR_INVALID_ARG, "key range [%lld, %lld) must lie within [0, Nkv=%lld]", (long long)kv_begin,
+                (long long)kv_end, (long long)Nkv);
+  if (dtype != ATTN_FP8_E4M3 && (descale_q || descale_k || descale_v))
+    return fail(ATTN_ERR_INVALID_ARG, "descales apply to ATTN_FP8_E4M3 only");
+  const Ranges r{kv_begin, kv_end, kv_end - kv_begin, 1, true, 0, 0};
+  return run_forward(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q, descale_k,
+                     descale_v, &r, stream);
+}
+
+int attn_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,
+               int64_t Hq, int64_t Nq, int64_t D, int out_dtype, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (!o_parts || !lse_parts || !o)
+    return fail(ATTN_ERR_INVALID_ARG, "o_parts, lse_parts and o must be non-NULL device pointers");
+  if (n_parts < 1 || B < 1 || Hq < 1 || Nq < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1 (n_parts=%lld B=%lld Hq=%lld Nq=%lld D=%lld)",
+                (long long)n_parts, (long long)B, (long long)Hq, (long long)Nq, (long long)D);
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "out_dtype must be ATTN_F32 or ATTN_BF16");
+  if (!aligned16(o_parts) || !aligned16(o) || (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "o_parts and o must be 16-byte aligned, lse_parts and lse 4-byte aligned");
+  if (D > 1024 || D % 32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: D must be a multiple of 32 in [32, 1024]", (long long)D);
+  if (n_parts > INT32_MAX || B * Hq * Nq >= ((int64_t)1 << 40))
+    return fail(ATTN_ERR_UNSUPPORTED, "too many parts or rows");
+  attn::MergeParams mp{};
+  mp.o_parts = o_parts;
+  mp.lse_parts = lse_parts;
+  mp.o = o;
+  mp.lse = lse;
+  mp.n_parts = (int)n_parts;
+  mp.D = (int)D;
+  mp.o_f32 = out_dtype == ATTN_F32 ? 1 : 0;
+  mp.rows = B * Hq * Nq;
+  mp.o_part_stride = mp.rows * D;
+  mp.lse_part_stride = mp.rows;
+  hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+size_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int64_t n_splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || D < 1 || n_splits < 1) return 0;
+  const int64_t rows = B * Hq * Nq;
+  // float32 partial O, then float32 partial LSE, each part 256-byte aligned
+  const int64_t o_bytes = (rows * D * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  return (size_t)(n_splits * (o_bytes + l_bytes));
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
+                     const float* descale_q, const float* descale_k, const float* descale_v, int64_t n_splits,
+                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_FP8_E4M3 && (descale_q || descale_k || descale_v))
+    return fail(ATTN_ERR_INVALID_ARG, "descales apply to ATTN_FP8_E4M3 only");
+  if (n_splits < 1 || n_splits > 4096) return fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [1, 4096]");
+  if (B < 1 || Hq < 1 || Nq < 1 || Nkv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1");
+  const size_t need = attn_splitkv_workspace_bytes(B, Hq, Nq, D, n_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be a device buffer of at least %zu bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t rows = B * Hq * Nq;
+  const int64_t o_bytes = (rows * D * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + n_splits * o_bytes);
+  // ranges of a multiple of 64 keys (whole tiles of every kernel); trailing
+  // ranges may be short or empty
+  const int64_t split_len = ((Nkv + n_splits - 1) / n_splits + 63) / 64 * 64;
+  const Ranges r{0, Nkv, split_len, n_splits, true, o_bytes / 4, l_bytes / 4};
+  int st = run_forward(q, k, v, o_parts, lse_parts, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q,
+                       descale_k, descale_v, &r, stream);
+  if (st != ATTN_OK) return st;
+  attn::MergeParams mp{};
+  mp.o_parts = o_parts;
+  mp.lse_parts = lse_parts;
+  mp.o = o;
+  mp.lse = lse;
+  mp.n_parts = (int)n_splits;
+  mp.D = (int)D;
+  mp.o_f32 = dtype == ATTN_F32 ? 1 : 0;
+  mp.rows = rows;
+  mp.o_part_stride = o_bytes / 4;
+  mp.lse_part_stride = l_bytes / 4;
+  hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
 }
 
 const char* attn_status_string(int status) {

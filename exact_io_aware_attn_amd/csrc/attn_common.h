@@ -144,6 +144,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four consecutive output elements at element index idx: float32 when
+// `f32` (partial results of a key range), otherwise bf16 (RNE).  idx is a
+// multiple of 4, so both stores are naturally aligned.
+__device__ __forceinline__ void store_o4(void* o, bool f32, int64_t idx, float a, float b, float c, float d) {
+  if (f32) {
+    *reinterpret_cast<f32x4*>((float*)o + idx) = f32x4{a, b, c, d};
+  } else {
+    const u32x2 pk = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    *reinterpret_cast<u32x2*>((__bf16*)o + idx) = pk;
+  }
+}
+
 // Decode four e4m3 codes (one dword, byte 0 first) to bf16, exactly
 // (every e4m3 value is representable in bf16).  Returns two packed dwords:
 // .x = (byte0 | byte1 << 16), .y = (byte2 | byte3 << 16) as bf16 pairs.

@@ -116,7 +116,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   const int h = lane >> 5;
 
   // ---- work decomposition --------------------------------------------------
-  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int wg_all = xcd_remap(blockIdx.x, p.total_wg);
+  const int per_split = p.total_wg / p.n_splits;
+  const int split = wg_all / per_split;  // key range (split-KV); 0 for a plain call
+  const int wg = wg_all - split * per_split;
+  const KeyRange kr = key_range(p, split);
   const int qt_raw = wg % p.n_qtiles;
   const int bh = wg / p.n_qtiles;
   const int hq = bh % p.Hq;
@@ -127,8 +131,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   const int q0w = q0 + wave * C::QW;
 
   const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
-  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
-  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * C::ES);
+  const int64_t kv_slab = (((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv + kr.k0) * D;
+  const uint32_t kv_bytes = (uint32_t)((int64_t)kr.nkv * D * C::ES);
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc((const char*)p.q + q_slab * C::ES, (uint32_t)((int64_t)p.Nq * D * C::ES));
   const i32x4 rk = sgpr_rsrc((const char*)p.k + kv_slab * C::ES, kv_bytes);
@@ -145,8 +149,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   }
 
   // ---- key range ------------------------------------------------------------------
-  int kv_end = p.Nkv;
-  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
+  int kv_end = kr.nkv;
+  if (p.causal) kv_end = min(kr.nkv, min(q0 + C::BR, p.Nq) + kr.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
   // ---- K/V staging ------------------------------------------------------------------
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = q0w + qb * 32 + l32;
-    klim[qb] = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
+    klim[qb] = p.causal ? min(kr.nkv - 1, qrow + kr.kv_off) : kr.nkv - 1;
   }
 
   int slot = 0;  // ring slot of tile kt
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 
     // ---- mask (tiles crossing the diagonal or the key tail only) ------------------
     const int key0 = kt * C::BC;
-    if ((key0 + C::BC > p.Nkv) || (p.causal && key0 + C::BC - 1 > q0w + p.kv_off)) {
+    if ((key0 + C::BC > kr.nkv) || (p.causal && key0 + C::BC - 1 > q0w + kr.kv_off)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -485,20 +489,18 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
     const float inv = l_tot > 0.0f ? out_scale / l_tot : 0.0f;
     const int qrow = q0w + qb * 32 + l32;
     if (qrow < p.Nq) {
-      const int64_t orow = q_slab + (int64_t)qrow * D;
+      const int64_t orow = split * p.o_split_stride + q_slab + (int64_t)qrow * D;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = db * 32 + 8 * g + 4 * h;
-          u32x2 pk;
-          pk.x = pack_bf16x2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv);
-          pk.y = pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d) = pk;
+          store_o4(p.o, p.o_f32, orow + d, acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv,
+                   acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
         }
       }
       if (p.lse != nullptr && h == 0)
-        p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
+        p.lse[split * p.lse_split_stride + ((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
             l_tot > 0.0f ? (m_run[qb] + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
@@ -509,7 +511,7 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   using C = PipeCfg<E, D, NW, NBUF, BC>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
+  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<E, D, NW, NBUF, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);

@@ -93,7 +93,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int wg_all = xcd_remap(blockIdx.x, p.total_wg);
+  const int per_split = p.total_wg / p.n_splits;
+  const int split = wg_all / per_split;  // key range (split-KV); 0 for a plain call
+  const int wg = wg_all - split * per_split;
+  const KeyRange kr = key_range(p, split);
   const int qt_raw = wg % p.n_qtiles;
   const int bh = wg / p.n_qtiles;
   const int hq = bh % p.Hq;
@@ -105,15 +109,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   const int qrow = q0w + l32;
 
   const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
-  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
-  const uint32_t kv_bytes = (uint32_t)((int64_t)p.Nkv * D * 2);
+  const int64_t kv_slab = (((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv + kr.k0) * D;
+  const uint32_t kv_bytes = (uint32_t)((int64_t)kr.nkv * D * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab, (uint32_t)((int64_t)p.Nq * D * 2));
   const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, kv_bytes);
   const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, kv_bytes);
   const float c = p.scale * kLog2e;
 
-  int kv_end = p.Nkv;
-  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + p.kv_off);
+  int kv_end = kr.nkv;
+  if (p.causal) kv_end = min(kr.nkv, min(q0 + C::BR, p.Nq) + kr.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
   uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
-  const int klim = p.causal ? min(p.Nkv - 1, qrow + p.kv_off) : p.Nkv - 1;
+  const int klim = p.causal ? min(kr.nkv - 1, qrow + kr.kv_off) : kr.nkv - 1;
 
   // K fragment: row l32, 16-byte chunk 4 cc + 2 dh + h.  The swizzle XORs
   // the low KB bits (KB = 3 or 4), so with G = 2^KB / 4 the address is
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] *= c;
     const int key0 = kt * C::BC;
-    if ((key0 + C::BC > p.Nkv) || (p.causal && key0 + C::BC - 1 > q0w + p.kv_off)) {
+    if ((key0 + C::BC > kr.nkv) || (p.causal && key0 + C::BC - 1 > q0w + kr.kv_off)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -309,20 +313,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < p.Nq) {
-    const int64_t orow = q_slab + (int64_t)qrow * D + dh * 32;
+    const int64_t orow = split * p.o_split_stride + q_slab + (int64_t)qrow * D + dh * 32;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 64 + 8 * g + 4 * h;
-        u32x2 pk;
-        pk.x = pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
-        pk.y = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d) = pk;
+        store_o4(p.o, p.o_f32, orow + d, acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                 acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
       }
     }
     if (p.lse != nullptr && dh == 0 && h == 0)
-      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
+      p.lse[split * p.lse_split_stride + ((int64_t)b * p.Hq + hq) * p.Nq + qrow] =
           l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -332,7 +334,7 @@ hipError_t launch_splitd(const FwdParams& p0, hipStream_t stream) {
   using C = SplitCfg<D>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
+  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
   hipLaunchKernelGGL((attn_fwd_splitd_kernel<D>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);

@@ -114,7 +114,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
   const int h = lane >> 5;
 
   // ---- work decomposition: (b, hq, query tile) ----------------------------
-  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int wg_all = xcd_remap(blockIdx.x, p.total_wg);
+  const int per_split = p.total_wg / p.n_splits;
+  const int split = wg_all / per_split;  // key range (split-KV); 0 for a plain call
+  const int wg = wg_all - split * per_split;
+  const KeyRange kr = key_range(p, split);
   const int qt_raw = wg % p.n_qtiles;
   const int bh = wg / p.n_qtiles;
   const int hq = bh % p.Hq;
@@ -126,13 +130,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
   const int qrow = q0w + l32;         // query row owned by this lane
 
   const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
-  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const int64_t kv_slab = (((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv + kr.k0) * D;
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc((const char*)p.q + q_slab * C::ES, (uint32_t)((int64_t)p.Nq * D * C::ES));
   const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc((const char*)p.k + kv_slab * C::ES, (uint32_t)((int64_t)p.Nkv * D * C::ES));
+      make_rsrc((const char*)p.k + kv_slab * C::ES, (uint32_t)((int64_t)kr.nkv * D * C::ES));
   const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc((const char*)p.v + kv_slab * C::ES, (uint32_t)((int64_t)p.Nkv * D * C::ES));
+      make_rsrc((const char*)p.v + kv_slab * C::ES, (uint32_t)((int64_t)kr.nkv * D * C::ES));
 
   // ---- scale: exp(x) = exp2(x * log2 e); fp8 folds the Q and K descales ---
   float qk_scale = p.scale * kLog2e;
@@ -172,10 +176,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
   }
 
   // ---- key range ------------------------------------------------------------
-  int kv_end = p.Nkv;
+  int kv_end = kr.nkv;
   if (p.causal) {
     const int last_row = min(q0 + C::BR, p.Nq) - 1;
-    kv_end = min(p.Nkv, last_row + p.kv_off + 1);
+    kv_end = min(kr.nkv, last_row + kr.kv_off + 1);
   }
   const int n_kt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
     }
 
     // ---- scale, mask, online softmax ------------------------------------------
-    const bool need_mask = (key0 + BC > p.Nkv) || (p.causal && key0 + BC - 1 > q0w + p.kv_off);
+    const bool need_mask = (key0 + BC > kr.nkv) || (p.causal && key0 + BC - 1 > q0w + kr.kv_off);
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NKB; ++nb) {
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
         float x = s[nb][r] * qk_scale;
         if (need_mask) {
           const int key = key0 + nb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool vis = key < p.Nkv && (!p.causal || key <= qrow + p.kv_off);
+          const bool vis = key < kr.nkv && (!p.causal || key <= qrow + kr.kv_off);
           x = vis ? x : -INFINITY;
         }
         s[nb][r] = x;
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.0f ? out_scale / l_tot : 0.0f;
   if (qrow < p.Nq) {
-    const int64_t orow = q_slab + (int64_t)qrow * D;
+    const int64_t orow = split * p.o_split_stride + q_slab + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -401,19 +405,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_tiled_kernel(FwdParams p) {
         const int d = db * 32 + 8 * g + 4 * h;
         const float o0 = acc[db][4 * g + 0] * inv, o1 = acc[db][4 * g + 1] * inv;
         const float o2 = acc[db][4 * g + 2] * inv, o3 = acc[db][4 * g + 3] * inv;
-        if constexpr (E == ELT_F32) {
-          *reinterpret_cast<f32x4*>((float*)p.o + orow + d) = f32x4{o0, o1, o2, o3};
-        } else {
-          u32x2 pk;
-          pk.x = pack_bf16x2(o0, o1);
-          pk.y = pack_bf16x2(o2, o3);
-          *reinterpret_cast<u32x2*>((__bf16*)p.o + orow + d) = pk;
-        }
+        store_o4(p.o, E == ELT_F32 || p.o_f32, orow + d, o0, o1, o2, o3);
       }
     }
     if (p.lse != nullptr && h == 0) {
       const float lse = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = lse;
+      p.lse[split * p.lse_split_stride + ((int64_t)b * p.Hq + hq) * p.Nq + qrow] = lse;
     }
   }
 }
@@ -423,7 +420,7 @@ hipError_t launch_tiled(const FwdParams& p0, hipStream_t stream) {
   using C = TiledCfg<E, D, NW, BC>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  const int64_t total = (int64_t)p.B * p.Hq * p.n_qtiles;
+  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
   hipLaunchKernelGGL((attn_fwd_tiled_kernel<E, D, NW, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);

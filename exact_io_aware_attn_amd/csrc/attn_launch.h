@@ -21,12 +21,40 @@ struct FwdParams {
   int causal;          // 0 or 1
   int kv_off;          // Nkv - Nq: key j visible to query i iff j <= i + kv_off
   int n_qtiles;        // filled by the launcher
-  int total_wg;        // filled by the launcher
+  int total_wg;        // filled by the launcher: n_splits * B * Hq * n_qtiles
   float scale;         // multiplier of Q K^T
   const float* dq;     // fp8 descales (device pointers) or null
   const float* dk;
   const float* dv;
+  // Key ranges (split-KV).  Split s of n_splits attends to the keys
+  // [kv_begin + s * split_len, min(kv_begin + (s + 1) * split_len, kv_end))
+  // of the Nkv-key sequence, with the causal alignment of the whole problem,
+  // and writes its own O (normalised over its range) and LSE at o +
+  // s * o_split_stride and lse + s * lse_split_stride (elements).  A plain
+  // call is one split over [0, Nkv).
+  int kv_begin;
+  int kv_end;
+  int split_len;
+  int n_splits;
+  int o_f32;                // O stored as float32 (partial results) instead of the dtype's output
+  int64_t o_split_stride;
+  int64_t lse_split_stride;
 };
+
+// The keys one work-group attends to: nkv keys starting at row k0 of its
+// (batch, KV head) slab; local key j is visible to query row i iff
+// j <= i + kv_off when causal.
+struct KeyRange {
+  int k0;
+  int nkv;
+  int kv_off;
+};
+
+__device__ __forceinline__ KeyRange key_range(const FwdParams& p, int split) {
+  const int k0 = p.kv_begin + split * p.split_len;
+  const int k1 = min(k0 + p.split_len, p.kv_end);
+  return KeyRange{k0, k1 > k0 ? k1 - k0 : 0, p.kv_off - k0};
+}
 
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 
@@ -44,5 +72,25 @@ LaunchFn wide_launcher(int elt, int D);
 
 // Launcher for the split-D kernels (bf16, 256 < D <= 1024), or nullptr.
 LaunchFn splitd_launcher(int elt, int D);
+
+// Log-sum-exp merge of partial results: part i of o_parts (rows, D) starts
+// at o_parts + i * o_part_stride and part i of lse_parts (rows) at
+// lse_parts + i * lse_part_stride, all float32 -> o (rows, D; float32 if
+// o_f32, else bf16) and lse (rows, or null).  D a multiple of 32 in
+// [32, 1024]; o_part_stride a multiple of 4.
+struct MergeParams {
+  const float* o_parts;
+  const float* lse_parts;
+  void* o;
+  float* lse;
+  int n_parts;
+  int D;
+  int o_f32;
+  int64_t rows;
+  int64_t o_part_stride;
+  int64_t lse_part_stride;
+};
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace attn

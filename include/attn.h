@@ -58,6 +58,7 @@
 #ifndef EXACT_IO_AWARE_ATTN_AMD_ATTN_H
 #define EXACT_IO_AWARE_ATTN_AMD_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -120,6 +121,77 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int causal, float scale,
                  const float* descale_q, const float* descale_k, const float* descale_v,
                  attn_stream_t stream);
+
+/*
+ * Key ranges and their merge (split-KV, chunked prefill, ring attention).
+ * ZYFA article, section "The details that make it production-grade": results
+ * computed over different key ranges merge consistently through the LSE,
+ * which is what chunked prefill requires.  For partial results (O_p, LSE_p)
+ * over disjoint key ranges, each normalised over its own range:
+ *     LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p.
+ */
+
+/*
+ * attn_fwd_partial -- attention over the keys kv_begin <= j < kv_end only.
+ *   q, k, v, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype: as attn_fwd; k and
+ *            v hold the whole Nkv-key sequence and the causal mask keeps the
+ *            whole problem's alignment (j <= i + Nkv - Nq, j the absolute key
+ *            index), so the partial results of a partition of [0, Nkv) merge
+ *            to attn_fwd's result.
+ *   descale_q, descale_k, descale_v: as attn_fwd_fp8 for ATTN_FP8_E4M3 (NULL
+ *            means 1.0); must be NULL for the other dtypes.
+ *   o_part : DEVICE float32 (B, Hq, Nq, D): O normalised over the range
+ *   lse_part: DEVICE float32 (B, Hq, Nq), required (not NULL)
+ *   kv_begin, kv_end: 0 <= kv_begin <= kv_end <= Nkv.  A row that sees no
+ *            key of the range gets O = 0 and LSE = -inf.
+ * Errors as attn_fwd; ATTN_ERR_INVALID_ARG also for a bad range or a NULL
+ * lse_part.
+ */
+int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     int causal, float scale, int dtype, int64_t kv_begin, int64_t kv_end,
+                     const float* descale_q, const float* descale_k, const float* descale_v,
+                     attn_stream_t stream);
+
+/*
+ * attn_merge -- merge n_parts partial results by their LSE (formula above).
+ *   o_parts  : DEVICE float32 (n_parts, B, Hq, Nq, D), 16-byte aligned
+ *   lse_parts: DEVICE float32 (n_parts, B, Hq, Nq); -inf marks a row that saw
+ *              no key in that part
+ *   o        : DEVICE output (B, Hq, Nq, D), float32 (out_dtype ATTN_F32) or
+ *              bfloat16 (ATTN_BF16), 16-byte aligned
+ *   lse      : DEVICE float32 (B, Hq, Nq), or NULL
+ *   D        : multiple of 32 in [32, 1024]
+ * Rows empty in every part get O = 0, LSE = -inf.  One kernel, enqueued on
+ * `stream`; nothing is allocated.
+ */
+int attn_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
+               int64_t B, int64_t Hq, int64_t Nq, int64_t D, int out_dtype, attn_stream_t stream);
+
+/* Bytes of device workspace attn_fwd_splitkv needs (0 for invalid sizes). */
+size_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int64_t n_splits);
+
+/*
+ * attn_fwd_splitkv -- attn_fwd computed as n_splits key ranges in ONE launch
+ * (n_splits times the work-groups, for problems whose B * Hq * query tiles
+ * leave compute units idle: few heads, long keys) followed by attn_merge.
+ *   Arguments as attn_fwd, plus:
+ *   descale_q, descale_k, descale_v: as attn_fwd_partial
+ *   n_splits : 1..4096; the keys are cut into ranges of
+ *              ceil(ceil(Nkv / n_splits) / 64) * 64 keys (the last ones may
+ *              be short or empty)
+ *   workspace, workspace_bytes: caller-owned DEVICE buffer, 256-byte aligned,
+ *              of at least attn_splitkv_workspace_bytes(...) bytes; it holds
+ *              the partial results, is overwritten, and must not be used by
+ *              other work until the merge on `stream` completes.
+ * The result equals attn_fwd's up to float32 rounding order.  Two kernels are
+ * enqueued on `stream`; nothing is allocated.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     int causal, float scale, int dtype,
+                     const float* descale_q, const float* descale_k, const float* descale_v,
+                     int64_t n_splits, void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* Static English name of a status code ("ATTN_OK", ...); never NULL. */
 const char* attn_status_string(int status);

@@ -85,3 +85,72 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(A, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(A.AttnError):
         A.lib()
+
+
+# ---------------------------------------------------------------------------
+# key ranges, merge and split-KV: validation only (every call below fails
+# before anything is enqueued)
+# ---------------------------------------------------------------------------
+
+def call_partial(lse=FAKE, kv_begin=0, kv_end=64, Nkv=64, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=2, Hkv=2, Nq=64, D=128, causal=0, scale=0.1,
+             dtype=A.ATTN_BF16)
+    a.update(kw)
+    return A.lib().attn_fwd_partial(a["q"], a["k"], a["v"], a["o"], lse, a["B"], a["Hq"], a["Hkv"], a["Nq"], Nkv,
+                                    a["D"], a["causal"], a["scale"], a["dtype"], kv_begin, kv_end,
+                                    a.get("dq"), None, None, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lse=None), dict(kv_begin=-1), dict(kv_begin=10, kv_end=5), dict(kv_end=65), dict(q=None),
+    dict(B=0), dict(Hq=3, Hkv=2), dict(dq=FAKE),                 # descale with a bf16 dtype
+    dict(dq=FAKE + 2, dtype=A.ATTN_FP8_E4M3),                    # misaligned descale
+])
+def test_partial_invalid_arguments(kw):
+    assert call_partial(**kw) == A.ATTN_ERR_INVALID_ARG
+    assert A.lib().attn_last_error() != b""
+
+
+def call_merge(o_parts=FAKE, lse_parts=FAKE, n_parts=2, o=FAKE, lse=None, B=1, Hq=2, Nq=16, D=128,
+               out_dtype=A.ATTN_BF16):
+    return A.lib().attn_merge(o_parts, lse_parts, n_parts, o, lse, B, Hq, Nq, D, out_dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(o_parts=None), dict(lse_parts=None), dict(o=None), dict(n_parts=0), dict(Nq=0), dict(D=0),
+    dict(out_dtype=A.ATTN_FP8_E4M3), dict(out_dtype=9), dict(o_parts=FAKE + 4), dict(o=FAKE + 8),
+    dict(lse_parts=FAKE + 2), dict(lse=FAKE + 1),
+])
+def test_merge_invalid_arguments(kw):
+    assert call_merge(**kw) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("D", [48, 1056])
+def test_merge_unsupported(D):
+    assert call_merge(D=D) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_splitkv_workspace_size():
+    f = A.lib().attn_splitkv_workspace_bytes
+    # per part: float32 O rounded up to 256 bytes, then float32 LSE likewise
+    assert f(1, 2, 3, 32, 1) == (1 * 2 * 3 * 32 * 4 + 255) // 256 * 256 + 256
+    assert f(2, 4, 100, 128, 5) == 5 * ((2 * 4 * 100 * 128 * 4 + 255) // 256 * 256 + (2 * 4 * 100 * 4 + 255) // 256 * 256)
+    assert f(0, 2, 3, 32, 1) == 0 and f(1, 2, 3, 32, 0) == 0
+
+
+def call_splitkv(n_splits=4, ws=FAKE, ws_bytes=1 << 40, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, D=128, causal=0,
+             scale=0.1, dtype=A.ATTN_BF16)
+    a.update(kw)
+    return A.lib().attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                    a["Nkv"], a["D"], a["causal"], a["scale"], a["dtype"], a.get("dq"), None, None,
+                                    n_splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_splits=0), dict(n_splits=5000), dict(ws=None), dict(ws_bytes=100), dict(ws=FAKE + 16),
+    dict(Nq=0), dict(q=None), dict(scale=float("nan")), dict(Hq=3, Hkv=2), dict(dq=FAKE),
+    dict(dq=FAKE + 2, dtype=A.ATTN_FP8_E4M3),
+])
+def test_splitkv_invalid_arguments(kw):
+    assert call_splitkv(**kw) == A.ATTN_ERR_INVALID_ARG
