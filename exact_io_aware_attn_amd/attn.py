@@ -230,7 +230,8 @@ def splitkv_workspace_bytes(B, Hq, Nq, D, n_splits):
     return int(lib().attn_splitkv_workspace_bytes(B, Hq, Nq, D, n_splits))
 
 
-def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, workspace=None, stream=None):
+def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, workspace=None, out=None, lse=None,
+                stream=None):
     """``fwd`` (or ``fwd_fp8`` with ``descales``) computed as ``n_splits`` key
     ranges in one launch plus a merge.
 
@@ -246,8 +247,10 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, work
     need = splitkv_workspace_bytes(B, Hq, Nq, D, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty((B, Hq, Nq, D), dtype=torch.float32 if dt == ATTN_F32 else torch.bfloat16, device=q.device)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    o = out if out is not None else torch.empty((B, Hq, Nq, D), dtype=torch.float32 if dt == ATTN_F32 else
+                                                torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     _check(lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, *dptr, int(n_splits),
                                   workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))

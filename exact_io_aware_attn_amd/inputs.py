@@ -95,6 +95,14 @@ WORKLOADS = {
     },
     # fp8 e4m3 diffusion-style attention with 1% outlier channels
     "fp8_outlier": Workload("fp8_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01),
+    # chunked prefill: a 256-token chunk against a 32K-token context, GQA,
+    # causal (bottom-right: the chunk sees the whole context and itself
+    # causally).  B * Hq * query tiles = 64 work-groups for 256 CUs, the case
+    # key-range splitting is for; the same problem run plainly and split into
+    # 16 key ranges (extra["n_splits"]) merged by LSE.
+    "chunk_prefill_bf16": Workload("chunk_prefill_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16"),
+    "chunk_prefill_splitkv_bf16": Workload("chunk_prefill_splitkv_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16",
+                                           extra={"n_splits": 16}),
 }
 
 
