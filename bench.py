@@ -136,7 +136,9 @@ def cpu_baseline(w, host_inp, n_heads, seconds):
         threads = 1
     G = w.Hq // w.Hkv
     rng = np.random.default_rng(1)
-    order = [(int(b), int(h)) for b, h in zip(rng.integers(w.B, size=4 * w.B * w.Hq), rng.integers(w.Hq, size=4 * w.B * w.Hq))]
+    # distinct (batch, head) slices in random order, until the budget or the
+    # whole workload is done
+    order = [(int(x // w.Hq), int(x % w.Hq)) for x in rng.permutation(w.B * w.Hq)]
     if w.dtype == "fp8":
         q8, k8, v8, desc = host_inp
 

@@ -40,10 +40,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float tot = 0.0f;
   const float* o_p = p.o_parts + row * p.D + d;
+  // four parts per step so that their loads are in flight together; an empty
+  // part (weight 0) contributes nothing even if its O is not finite
+#pragma unroll 4
   for (int i = 0; i < p.n_parts; ++i) {
     const float w = exp2_fast((lse_p[i * p.lse_part_stride] - m_safe) * kLog2e);  // 0 for an empty part
+    const f32x4 x = *reinterpret_cast<const f32x4*>(o_p + i * p.o_part_stride);
     tot += w;
-    if (w != 0.0f) acc += w * *reinterpret_cast<const f32x4*>(o_p + i * p.o_part_stride);
+    acc += w != 0.0f ? w * x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   store_o4(p.o, p.o_f32, row * p.D + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);

@@ -99,10 +99,11 @@ WORKLOADS = {
     # causal (bottom-right: the chunk sees the whole context and itself
     # causally).  B * Hq * query tiles = 64 work-groups for 256 CUs, the case
     # key-range splitting is for; the same problem run plainly and split into
-    # 16 key ranges (extra["n_splits"]) merged by LSE.
+    # 8 key ranges (extra["n_splits"]; 512 work-groups, two per CU, the best
+    # of 1..64 measured) merged by LSE.
     "chunk_prefill_bf16": Workload("chunk_prefill_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16"),
     "chunk_prefill_splitkv_bf16": Workload("chunk_prefill_splitkv_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16",
-                                           extra={"n_splits": 16}),
+                                           extra={"n_splits": 8}),
 }
 
 

@@ -158,3 +158,31 @@ def test_splitkv_matches_plain_call():
     assert (l1 - l2).abs().max().item() <= 1e-3 * max(1.0, l1.abs().max().item())
     assert torch.equal(o2.view(torch.int16), o3.view(torch.int16))
     assert torch.equal(l2.view(torch.int32), l3.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["chunk_prefill_splitkv_bf16", "chunk_prefill_bf16"])
+def test_chunk_prefill_full_size_sampled(name):
+    """The bench's chunked-prefill workloads at full size, in the launch
+    configuration it times (split into extra["n_splits"] key ranges or not),
+    against the oracle on sampled rows of a few heads."""
+    from exact_io_aware_attn_amd.inputs import WORKLOADS
+    w = WORKLOADS[name]
+    note(f"{name} full size, sampled rows")
+    (q, k, v), _, _ = gpu_and_oracle_inputs(w)
+    ns = int(w.extra.get("n_splits", 0))
+    if ns:
+        o, lse = A.fwd_splitkv(q, k, v, ns, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = A.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O = o.float().cpu().double().numpy()
+    L = lse.cpu().double().numpy()
+    assert np.isfinite(O).all() and not np.isnan(L).any()
+    qh, kh, vh = (t.cpu() for t in (q, k, v))
+    rng = np.random.default_rng(5)
+    G = w.Hq // w.Hkv
+    for b, hq in [(0, 0), (w.B - 1, w.Hq - 1), (0, int(rng.integers(w.Hq)))]:
+        rows = np.unique(np.concatenate([[0, w.Nq - 1], rng.integers(0, w.Nq, 40)]))
+        Oref, Lref = oracle.attention_head(qh[b, hq].double().numpy(), kh[b, hq // G].double().numpy(),
+                                           vh[b, hq // G].double().numpy(), w.scale, w.causal, rows=rows)
+        check(O[b, hq][rows], L[b, hq][rows], Oref, Lref, TOL_O[w.dtype])
