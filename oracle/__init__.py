@@ -16,6 +16,9 @@ e4m3           -- decoding of OCP FP8 E4M3FN codes to exact float64 values.
 keyrange       -- attention over one range of the keys (causal alignment of the
                   whole problem) and the log-sum-exp merge of such partial
                   results (split-KV, chunked prefill).
+quant          -- the fp8 input pipeline: signed Hadamard rotation of Q and K,
+                  e4m3 encoding (nearest, ties to even, saturating) and
+                  quantisation with one descale per 64-row block.
 
 Every function cites the passage of the source pages it follows, by page title
 and section.  No function here is "parity unpinned": each one is pinned by a
@@ -26,6 +29,7 @@ from .exact import attention, attention_head, kv_head_of, visible_mask
 from .online import online_attention_head
 from .e4m3 import e4m3fn_decode, E4M3FN_MAX
 from .keyrange import attention_range, attention_range_head, key_range_mask, merge
+from .quant import dequantize_blocks, e4m3fn_encode, hadamard, quantize_blocks, rotation
 
 __all__ = [
     "attention",
@@ -39,4 +43,9 @@ __all__ = [
     "attention_range_head",
     "key_range_mask",
     "merge",
+    "e4m3fn_encode",
+    "hadamard",
+    "rotation",
+    "quantize_blocks",
+    "dequantize_blocks",
 ]

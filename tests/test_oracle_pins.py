@@ -21,6 +21,7 @@ import torch
 import oracle
 import oracle.exact as oatt
 import oracle.keyrange as omerge
+import oracle.quant as oquant
 from oracle import attention, attention_head, e4m3fn_decode, online_attention_head
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -324,11 +325,93 @@ def check_merge_edge_cases():
     return bool(ok)
 
 
+def check_e4m3_encode_library():
+    """e4m3fn encoding against torch's float8_e4m3fn cast (an independent
+    implementation), over normals, subnormals, signed zeros and exact
+    midpoints between neighbouring codes."""
+    rng = np.random.default_rng(700)
+    vals = [rng.standard_normal(20000) * 50, rng.standard_normal(5000) * 2.0 ** -8,
+            np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, -(2.0 ** -10), 2.0 ** -6])]
+    mids = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    vals.append((mids[1:] + mids[:-1]) / 2)
+    vals.append(-(mids[1:] + mids[:-1]) / 2)
+    x = np.clip(np.concatenate(vals), -448, 448).astype(np.float32)
+    ours = oquant.e4m3fn_encode(x)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return bool(np.array_equal(ours, lib))
+
+
+def check_e4m3_encode_definition():
+    """Every finite code round-trips; midpoints go to the even code; values
+    past 448 saturate."""
+    c = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3fn_decode(c)
+    fin = ~np.isnan(v)
+    ok = np.array_equal(oquant.e4m3fn_encode(v[fin]), c[fin])
+    # 1.0 (0x38) .. 1.125 (0x39) .. 1.25 (0x3A): midpoints go to 0x38 and 0x3A
+    ok &= oquant.e4m3fn_encode(np.array([1.0625]))[0] == 0x38
+    ok &= oquant.e4m3fn_encode(np.array([1.1875]))[0] == 0x3A
+    ok &= oquant.e4m3fn_encode(np.array([1.07]))[0] == 0x39
+    ok &= bool(np.all(oquant.e4m3fn_encode(np.array([449.0, 1e6])) == 0x7E))
+    ok &= oquant.e4m3fn_encode(np.array([-1e6]))[0] == 0xFE
+    return bool(ok)
+
+
+def check_hadamard_and_rotation():
+    """Sylvester matrices equal scipy's; the signed, normalised rotation is
+    orthogonal and leaves every score q . k (so attention) unchanged."""
+    import scipy.linalg
+    ok = True
+    for D in (1, 2, 8, 64, 128, 256):
+        ok &= np.array_equal(oquant.hadamard(D), scipy.linalg.hadamard(D).astype(np.float64))
+    rng = np.random.default_rng(701)
+    for D in (64, 128):
+        signs = rng.choice([-1.0, 1.0], size=D)
+        R = oquant.rotation(signs)
+        ok &= np.allclose(R @ R.T, np.eye(D), rtol=0, atol=1e-12)
+        q, k, v = rng_arrays(702 + D, (1, 2, 9, D), (1, 2, 11, D), (1, 2, 11, D))
+        O, L = attention(q, k, v, 0.2, True)
+        O2, L2 = attention(q @ R, k @ R, v, 0.2, True)
+        ok &= np.allclose(O, O2, rtol=0, atol=1e-12) and np.allclose(L, L2, rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def check_block_quantization():
+    """Block descales: amax / 448 per 64-row block (ragged last block), the
+    largest code of a nonzero block decodes to +-448, all-zero blocks give
+    descale 1 and code 0, and every value is within half an e4m3 step of its
+    dequantised value."""
+    rng = np.random.default_rng(703)
+    x = rng.standard_normal((2, 3, 150, 32)) * np.array([1.0, 10.0, 0.01])[None, :, None, None]
+    x[1, 2, 64:128] = 0.0
+    x = x.astype(np.float32).astype(np.float64)
+    codes, desc = oquant.quantize_blocks(x)
+    ok = desc.shape == (2, 3, 3) and codes.shape == x.shape
+    dq = oquant.dequantize_blocks(codes, desc)
+    for b in range(2):
+        for h in range(3):
+            for i in range(3):
+                blk = x[b, h, 64 * i:64 * i + 64]
+                amax = np.abs(blk).max()
+                dec = oracle.e4m3fn_decode(codes[b, h, 64 * i:64 * i + 64])
+                if amax == 0:
+                    ok &= desc[b, h, i] == 1.0 and np.all(codes[b, h, 64 * i:64 * i + 64] & 0x7F == 0)
+                    continue
+                ok &= desc[b, h, i] == np.float32(np.float32(amax) / np.float32(448.0))
+                ok &= np.abs(dec).max() == 448.0
+                err = np.abs(dq[b, h, 64 * i:64 * i + 64] - blk)
+                # half a step: 2^-4 relative for normals, 2^-10 absolute (x descale) for subnormals
+                bound = np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * desc[b, h, i]) * (1 + 1e-6)
+                ok &= bool(np.all(err <= bound))
+    return bool(ok)
+
+
 ALL_CHECKS = [check_golden, check_brute_force, check_library_sdpa, check_rows_sum_to_one,
               check_identical_keys, check_one_hot, check_row_shift, check_causal_prefix,
               check_gqa_repeat, check_merge, check_permutations, check_no_visible_rows,
               check_rows_subset, check_range_brute_force, check_range_partition_merges_to_whole,
-              check_merge_edge_cases]
+              check_merge_edge_cases, check_e4m3_encode_library, check_e4m3_encode_definition,
+              check_hadamard_and_rotation, check_block_quantization]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -446,6 +529,41 @@ def _mut_merge_max_lse(O_parts, LSE_parts):
     return O, np.asarray(LSE_parts, dtype=np.float64).max(axis=0)
 
 
+_real_encode = oquant.e4m3fn_encode
+_real_hadamard = oquant.hadamard
+
+
+def _mut_encode_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    vals = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    hi = np.clip(np.searchsorted(vals, a), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    code = np.where(vals[hi] - a <= a - vals[lo], hi, lo).astype(np.uint8)  # ties away from zero
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _mut_encode_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    vals = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    code = np.clip(np.searchsorted(vals, a, side="right") - 1, 0, 0x7E).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _mut_hadamard_unsigned_second_half(D):
+    # the last Sylvester step forgets to negate the lower-right block
+    H = _real_hadamard(D)
+    if D > 1:
+        H[D // 2:, D // 2:] = H[:D // 2, :D // 2]
+    return H
+
+
+def _mut_rotation_unnormalised(signs):
+    signs = np.asarray(signs, dtype=np.float64)
+    return signs[:, None] * oquant.hadamard(signs.shape[0])
+
+
 MUTATIONS = {
     "gqa_modulo": (oatt, "kv_head_of", _mut_gqa),
     "causal_top_left": (oatt, "visible_mask", _mut_topleft),
@@ -458,6 +576,10 @@ MUTATIONS = {
     "range_causal_relative": (omerge, "key_range_mask", _mut_range_relative_causal),
     "merge_mean": (omerge, "merge", _mut_merge_mean),
     "merge_lse_max": (omerge, "merge", _mut_merge_max_lse),
+    "e4m3_ties_away": (oquant, "e4m3fn_encode", _mut_encode_ties_away),
+    "e4m3_truncate": (oquant, "e4m3fn_encode", _mut_encode_truncate),
+    "hadamard_wrong_block": (oquant, "hadamard", _mut_hadamard_unsigned_second_half),
+    "rotation_unnormalised": (oquant, "rotation", _mut_rotation_unnormalised),
 }
 
 
