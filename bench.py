@@ -1,7 +1,10 @@
 """Benchmark of the exact attention forward on one MI355X.
 
-One step = one forward pass (one ``attn_fwd`` launch) over the whole batch of
-the workload, inputs resident in HBM.  Prints ONE JSON line.
+One step = one forward pass over the whole batch of the workload (one
+``attn_fwd`` launch; the partial-attention and merge launches of a key-range
+split; or the block quantisation of Q, K and V followed by the block-scaled
+e4m3 attention of the fp8 input pipeline), inputs resident in HBM.  Prints ONE
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -15,8 +18,9 @@ same point about sustained clocks).
 Throughput is matmul TFLOP/s: 4 * B * Hq * D * (visible query/key pairs) per
 step (the QK^T and PV products; softmax work is not counted).  The roofline
 object prices the same flops against the dense MFMA peak of the compute dtype,
-using the kernel's own average duration from HIP events recorded on the
-launch stream.  The cpu_baseline object times the fp64 oracle on a bounded
+using the attention kernel's own average duration from HIP events recorded
+on the launch stream around that launch (around the whole step for a key-range
+split, whose merge launch is then counted too).  The cpu_baseline object times the fp64 oracle on a bounded
 sample of the same workload on the host cores.
 """
 import argparse
@@ -37,6 +41,11 @@ METRIC = "attention fwd TFLOPS on 1 MI355X and % of dense bf16/fp8 MFMA peak"
 # MI355X dense MFMA peaks (TFLOP/s): bf16 2.5 PF, fp8 5.0 PF, fp32 157.3 TF.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "prefill_causal_bf16"
+INPUTS = {
+    "fp8": "i.i.d. N(0,1), 1% outlier channels x8, per-tensor e4m3, seed 0",
+    "fp8blk": "bf16 i.i.d. N(0,1), 1% outlier channels x8 shared by Q and K, seed 0; "
+              "quantised on the device, one descale per 64 rows, Q and K Hadamard-rotated",
+}
 
 
 # HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE per
@@ -100,6 +109,8 @@ def copy_calibration(mib, steps):
 
 def gpu_inputs(w, dev):
     inp = make_inputs(w)
+    if w.dtype == "fp8blk":
+        return tuple(t.to(dev) for t in inp), inp
     if w.dtype == "fp8":
         q8, k8, v8, desc = inp
         ds = [torch.tensor([float(x)], dtype=torch.float32, device=dev) for x in desc]
@@ -108,6 +119,40 @@ def gpu_inputs(w, dev):
 
 
 def make_step(w, dev_inp, out, lse):
+    """A callable running one step; called with a pair of events it records
+    them around the step's dominant kernel on the launch stream."""
+    stream = torch.cuda.current_stream()
+
+    def bracket(fn):
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fn()
+            if ev is not None:
+                ev[1].record(stream)
+        return step
+
+    if w.dtype == "fp8blk":
+        # the fp8 input pipeline: Q and K rotated and block-quantised, V
+        # block-quantised, then block-scaled e4m3 attention; buffers once
+        q, k, v, signs = dev_inp
+        bufs = []
+        for t in (q, k, v):
+            nb = (t.shape[2] + 63) // 64
+            bufs.append((torch.empty(t.shape, dtype=torch.float8_e4m3fn, device=t.device),
+                         torch.empty((t.shape[0], t.shape[1], nb), dtype=torch.float32, device=t.device)))
+        (cq, dq), (ck, dk), (cv, dv) = bufs
+
+        def step(ev=None):
+            A.quantize_fp8(q, signs, codes=cq, descales=dq)
+            A.quantize_fp8(k, signs, codes=ck, descales=dk)
+            A.quantize_fp8(v, None, codes=cv, descales=dv)
+            if ev is not None:
+                ev[0].record(stream)
+            A.fwd_fp8_blocks(cq, ck, cv, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse)
+            if ev is not None:
+                ev[1].record(stream)
+        return step
     if w.extra.get("n_splits"):
         # key-range split: one launch over all ranges, then the LSE merge,
         # through attn_fwd_splitkv with a workspace allocated once, here
@@ -116,13 +161,13 @@ def make_step(w, dev_inp, out, lse):
         desc = tuple(dev_inp[3:]) if w.dtype == "fp8" else None
         ws = torch.empty(A.splitkv_workspace_bytes(w.B, w.Hq, w.Nq, w.D, ns), dtype=torch.uint8, device=q.device)
 
-        return lambda: A.fwd_splitkv(q, k, v, ns, causal=w.causal, scale=w.scale, descales=desc, workspace=ws,
-                                     out=out, lse=lse)
+        return bracket(lambda: A.fwd_splitkv(q, k, v, ns, causal=w.causal, scale=w.scale, descales=desc,
+                                             workspace=ws, out=out, lse=lse))
     if w.dtype == "fp8":
         q, k, v, dq, dk, dv = dev_inp
-        return lambda: A.fwd_fp8(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse)
+        return bracket(lambda: A.fwd_fp8(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse))
     q, k, v = dev_inp
-    return lambda: A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)
+    return bracket(lambda: A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse))
 
 
 def cpu_baseline(w, host_inp, n_heads, seconds):
@@ -139,7 +184,18 @@ def cpu_baseline(w, host_inp, n_heads, seconds):
     # distinct (batch, head) slices in random order, until the budget or the
     # whole workload is done
     order = [(int(x // w.Hq), int(x % w.Hq)) for x in rng.permutation(w.B * w.Hq)]
-    if w.dtype == "fp8":
+    if w.dtype == "fp8blk":
+        q, k, v, signs = host_inp
+        s = signs.numpy()
+
+        def blk(t, b, h, sg):
+            # blocks never span heads: one head's slab quantises alone exactly
+            x = t[b:b + 1, h:h + 1].to(torch.float64).numpy()
+            return oracle.dequantize_blocks(*oracle.quantize_blocks(x, sg))[0, 0]
+        get_q = lambda b, h: blk(q, b, h, s)
+        get_k = lambda b, h: blk(k, b, h, s)
+        get_v = lambda b, h: blk(v, b, h, None)
+    elif w.dtype == "fp8":
         q8, k8, v8, desc = host_inp
 
         def head(t, d, b, h):
@@ -214,10 +270,8 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
+    for pair in ev:
+        step(pair)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in ev]
@@ -227,7 +281,8 @@ def main():
     flops = float(w.flops)
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_kernel_s / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    compute_dtype = "fp8" if w.dtype == "fp8blk" else w.dtype
+    peak = PEAK_TFLOPS[compute_dtype]
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -239,12 +294,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": compute_dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
-            "causal": w.causal, "scale": "1/sqrt(D)", "inputs": "i.i.d. N(0,1), seed 0",
+            "causal": w.causal, "scale": "1/sqrt(D)", "inputs": INPUTS.get(w.dtype, "i.i.d. N(0,1), seed 0"),
+            **({"timed": "block quantisation of Q, K (rotated) and V + block-scaled e4m3 attention; "
+                         "roofline on the attention launch alone"} if w.dtype == "fp8blk" else {}),
             **({"n_splits": int(w.extra["n_splits"]),
                 "timed": "partial-attention launch over all key ranges + LSE merge launch"}
                if w.extra.get("n_splits") else {}),

@@ -19,7 +19,8 @@ ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/attn.h declares
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
-            "attn_fwd_splitkv", "attn_status_string", "attn_last_error", "attn_version")
+            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_status_string",
+            "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +57,10 @@ def lib():
     L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, vp, vp, vp,
                                    i64, vp, ctypes.c_size_t, vp]
     L.attn_fwd_splitkv.restype = ci
+    L.attn_quantize_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp]
+    L.attn_quantize_fp8.restype = ci
+    L.attn_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
+    L.attn_fwd_fp8_blocks.restype = ci
     L.attn_status_string.argtypes = [ci]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -255,3 +260,54 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, work
                                   B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, *dptr, int(n_splits),
                                   workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
     return o, lse
+
+
+def quantize_fp8(x, signs=None, codes=None, descales=None, stream=None):
+    """Block e4m3 quantisation of a bf16 (B, H, N, D) device tensor, one
+    descale per 64 rows, rows rotated by diag(signs) H_D / sqrt(D) first if
+    ``signs`` (an int8 device tensor of D values +-1) is given.  Returns
+    (codes as torch.float8_e4m3fn, descales float32 (B, H, ceil(N/64)))."""
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 (B, H, N, D) device tensor")
+    B, H, N, D = x.shape
+    sp = None
+    if signs is not None:
+        if signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != D:
+            raise ValueError("signs must be an int8 device tensor of D values")
+        sp = signs.data_ptr()
+    if codes is None:
+        codes = torch.empty((B, H, N, D), dtype=torch.float8_e4m3fn, device=x.device)
+    if descales is None:
+        descales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
+    if codes.dtype != torch.float8_e4m3fn or tuple(codes.shape) != (B, H, N, D) or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous float8_e4m3fn tensor of x's shape")
+    if descales.dtype != torch.float32 or tuple(descales.shape) != (B, H, (N + 63) // 64):
+        raise ValueError("descales must be float32 of shape (B, H, ceil(N/64))")
+    desc = descales
+    _check(lib().attn_quantize_fp8(x.data_ptr(), codes.data_ptr(), desc.data_ptr(), B, H, N, D, sp,
+                                   _stream_ptr(stream)))
+    return codes, desc
+
+
+def fwd_fp8_blocks(q, k, v, dq_blocks, dk_blocks, dv_blocks, causal=False, scale=None, out=None, lse=None,
+                   return_lse=True, stream=None):
+    """Exact attention on e4m3 inputs with one descale per 64-row block (the
+    layout ``quantize_fp8`` returns).  bf16 output, float32 LSE."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    for t in (q, k, v):
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError("fwd_fp8_blocks takes torch.float8_e4m3fn tensors")
+    for d, H, N in ((dq_blocks, Hq, Nq), (dk_blocks, Hkv, Nkv), (dv_blocks, Hkv, Nkv)):
+        if d.dtype != torch.float32 or not d.is_cuda or tuple(d.shape) != (B, H, (N + 63) // 64):
+            raise ValueError("block descales must be float32 device tensors of shape (B, H, ceil(N/64))")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd_fp8_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D,
+                                     int(causal), float(scale), dq_blocks.data_ptr(), dk_blocks.data_ptr(),
+                                     dv_blocks.data_ptr(), _stream_ptr(stream)))
+    return out, lse

@@ -34,7 +34,8 @@ struct Ranges {
 
 int run_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
-                const float* dq, const float* dk, const float* dv, const Ranges* ranges, attn_stream_t stream) {
+                const float* dq, const float* dk, const float* dv, const Ranges* ranges, attn_stream_t stream,
+                bool blk_scaled = false) {
   g_last_error[0] = '\0';
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL device pointers");
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
@@ -74,7 +75,14 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   // generic tiled kernel and every other D > 256 case on the split-D kernels;
   // both scale before masking.
   attn::LaunchFn fn = nullptr;
-  if (scale > 0.0f) fn = attn::wide_launcher(elt, (int)D);
+  if (blk_scaled) {
+    // block descales: the e4m3 direct-to-LDS kernel only
+    if (scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
+    if (!fn)
+      return fail(ATTN_ERR_UNSUPPORTED, "block-scaled e4m3 needs D in {64, 128, 256} and scale > 0 (D=%lld)",
+                  (long long)D);
+  }
+  if (!fn && scale > 0.0f) fn = attn::wide_launcher(elt, (int)D);
   if (!fn && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
   if (!fn) fn = D <= 256 ? attn::tiled_launcher(elt, (int)D) : attn::splitd_launcher(elt, (int)D);
   if (!fn)
@@ -116,6 +124,7 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
     p.o_split_stride = 0;
     p.lse_split_stride = 0;
   }
+  p.blk_scaled = blk_scaled ? 1 : 0;
   hipError_t err = fn(p, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return ATTN_OK;
@@ -186,6 +195,41 @@ int attn_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, vo
   hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
   return ATTN_OK;
+}
+
+int attn_quantize_fp8(const void* x, void* codes, float* descales, int64_t B, int64_t H, int64_t N, int64_t D,
+                      const int8_t* signs, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (!x || !codes || !descales) return fail(ATTN_ERR_INVALID_ARG, "x, codes and descales must be non-NULL device pointers");
+  if (B < 1 || H < 1 || N < 1 || D < 1) return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(descales) & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "x and codes must be 16-byte aligned, descales 4-byte aligned");
+  if (D != 64 && D != 128 && D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the quantiser takes D = 64, 128 or 256", (long long)D);
+  if (B * H > INT32_MAX || N * D * 2 >= ((int64_t)1 << 31) || B * H * ((N + 63) / 64) >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+  attn::QuantParams qp{};
+  qp.x = static_cast<const __bf16*>(x);
+  qp.codes = static_cast<uint8_t*>(codes);
+  qp.descales = descales;
+  qp.signs = signs;
+  qp.S = (int)(B * H);
+  qp.N = (int)N;
+  qp.D = (int)D;
+  hipError_t err = attn::launch_quant_fp8(qp, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "quantiser launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+int attn_fwd_fp8_blocks(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale,
+                        const float* dq_blocks, const float* dk_blocks, const float* dv_blocks,
+                        attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dq_blocks || !dk_blocks || !dv_blocks)
+    return fail(ATTN_ERR_INVALID_ARG, "dq_blocks, dk_blocks and dv_blocks must be non-NULL device pointers");
+  return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_FP8_E4M3, dq_blocks, dk_blocks,
+                     dv_blocks, nullptr, stream, true);
 }
 
 size_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int64_t n_splits) {

@@ -138,6 +138,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// A float the whole wave reads from one address, through the scalar cache
+// (a load from the constant address space; the data must not change while
+// the kernel runs).
+__device__ __forceinline__ float load_scalar(const float* ptr, int64_t i) {
+  using cfloat = const __attribute__((address_space(4))) float;
+  return ((cfloat*)(uintptr_t)ptr)[i];
+}
+
 // Round two floats to bf16 (RNE) and pack them, first in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};

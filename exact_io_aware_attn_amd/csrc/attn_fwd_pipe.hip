@@ -141,11 +141,23 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
 
   // exp(x) = exp2(x log2 e); e4m3 folds the Q and K descales in here and the
   // V descale into 1/l.  Positive (the launcher routes other scales elsewhere).
+  // With one descale per 64-row block (FA blog, "FA3 — el momento Hopper":
+  // a scale per 64 x d tile), this wave's 32 query rows lie in one Q block
+  // and each key tile in one K/V block: the Q and K block descales fold into
+  // the tile's exp2 multiplier and the V block descale into the exponent
+  // (P is formed already multiplied by it) and into the tile's row sum.
   float c = p.scale * kLog2e;
   float out_scale = 1.0f;
+  int64_t kv_blk0 = 0;   // first K/V block descale of this (batch, KV head)
   if constexpr (FP8) {
-    c *= (p.dq ? p.dq[0] : 1.0f) * (p.dk ? p.dk[0] : 1.0f);
-    out_scale = p.dv ? p.dv[0] : 1.0f;
+    if (p.blk_scaled) {
+      const int nqb = (p.Nq + 63) / 64;
+      c *= p.dq[((int64_t)b * p.Hq + hq) * nqb + min(q0w, p.Nq - 1) / 64];
+      kv_blk0 = ((int64_t)b * p.Hkv + hk) * ((p.Nkv + 63) / 64);
+    } else {
+      c *= (p.dq ? p.dq[0] : 1.0f) * (p.dk ? p.dk[0] : 1.0f);
+      out_scale = p.dv ? p.dv[0] : 1.0f;
+    }
   }
 
   // ---- key range ------------------------------------------------------------------
@@ -277,6 +289,17 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
     klim[qb] = p.causal ? min(kr.nkv - 1, qrow + kr.kv_off) : kr.nkv - 1;
   }
 
+  // Block descales of the K/V tiles: scalar loads one tile ahead, taken up
+  // right after the loop-top barrier, whose wait already covers them (a
+  // vector load would be waited for behind the in-flight tile loads).
+  float dk_nx = 1.0f, dv_nx = 1.0f;
+  if constexpr (FP8) {
+    if (p.blk_scaled && n_kt > 0) {
+      dk_nx = load_scalar(p.dk, kv_blk0 + kr.k0 / 64);
+      dv_nx = load_scalar(p.dv, kv_blk0 + kr.k0 / 64);
+    }
+  }
+
   int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
     // Tile kt is resident once at most the loads of the NBUF-2 later tiles
@@ -287,6 +310,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
     else
       wait_vmem_all();
     __syncthreads();
+    // this tile's exp2 multiplier, log2 of the V factor in P, 1 / that factor
+    float ct = c, lg_v = 0.0f, inv_v = 1.0f;
+    if constexpr (FP8) {
+      if (p.blk_scaled) {
+        ct = c * dk_nx;
+        lg_v = __builtin_amdgcn_logf(dv_nx);
+        inv_v = __builtin_amdgcn_rcpf(dv_nx);
+        asm volatile("" ::"v"(ct), "v"(lg_v), "v"(inv_v));
+        if (kt + 1 < n_kt) {
+          const int64_t kblk = kv_blk0 + (kr.k0 + (kt + 1) * C::BC) / 64;
+          dk_nx = load_scalar(p.dk, kblk);
+          dv_nx = load_scalar(p.dv, kblk);
+        }
+      }
+    }
     const int nslot = slot == 0 ? NBUF - 1 : slot - 1;  // slot of tile kt-1, free now
     if constexpr (FP8) {
       // V tile kt+1 (in registers since the last iteration) into its slot,
@@ -401,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
-      const float mrow = max_halves(mx) * c;  // scaled (base-2) units
+      const float mrow = max_halves(mx) * ct;  // scaled (base-2) units
       if (__builtin_amdgcn_ballot_w64(mrow > m_run[qb] + kTau) != 0) {
         // rows that have seen no visible key yet keep m = -inf; exp2 of
         // (-inf) - 0 is 0 there, never (-inf) - (-inf)
@@ -417,21 +455,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         l_run[qb] *= alpha;
         m_run[qb] = m_new;
       }
-      const float mneg = m_run[qb] == -INFINITY ? 0.0f : -m_run[qb];
-      float ls = l_run[qb];
+      const float mneg = (m_run[qb] == -INFINITY ? 0.0f : -m_run[qb]) + lg_v;
+      float ls = FP8 ? 0.0f : l_run[qb];
 #pragma unroll
       for (int s16 = 0; s16 < 2 * C::NKB; ++s16) {
         const int kb = s16 >> 1, r0 = (s16 & 1) * 8;
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(s[qb][kb][r0 + i], c, mneg));
+        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(s[qb][kb][r0 + i], ct, mneg));
         pf[qb][s16].x = pack_bf16x2(e[0], e[1]);
         pf[qb][s16].y = pack_bf16x2(e[2], e[3]);
         pf[qb][s16].z = pack_bf16x2(e[4], e[5]);
         pf[qb][s16].w = pack_bf16x2(e[6], e[7]);
         ls += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
-      l_run[qb] = ls;
+      l_run[qb] = FP8 ? __builtin_fmaf(ls, inv_v, l_run[qb]) : ls;
     }
 
     // ---- O^T += V^T P^T ---------------------------------------------------------------

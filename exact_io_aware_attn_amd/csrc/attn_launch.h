@@ -39,6 +39,9 @@ struct FwdParams {
   int o_f32;                // O stored as float32 (partial results) instead of the dtype's output
   int64_t o_split_stride;
   int64_t lse_split_stride;
+  // e4m3 with one descale per 64-row block (a plain key range only): dq
+  // points at (B, Hq, ceil(Nq/64)) floats, dk and dv at (B, Hkv, ceil(Nkv/64))
+  int blk_scaled;
 };
 
 // The keys one work-group attends to: nkv keys starting at row k0 of its
@@ -92,5 +95,18 @@ struct MergeParams {
 };
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+// e4m3 block quantisation of S = B * H slabs of N x D bf16 rows (D = 64,
+// 128 or 256): codes (S, N, D), descales (S, ceil(N/64)); rows rotated by
+// diag(signs) H_D / sqrt(D) first when signs (D values of +-1) is not null.
+struct QuantParams {
+  const __bf16* x;
+  uint8_t* codes;
+  float* descales;
+  const int8_t* signs;
+  int S, N, D;
+};
+
+hipError_t launch_quant_fp8(const QuantParams& p, hipStream_t stream);
 
 }  // namespace attn

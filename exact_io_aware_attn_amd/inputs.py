@@ -19,6 +19,12 @@ Q, K, V multiplies round(0.01 * H * D) distinct (head, channel) columns by 8
 (the "1% outlier channels" of the diffusion-style fp8 workload; a channel is
 read as one of the H*D hidden features), then quantises each tensor with
 descale = absmax / 448 (float32) and code = e4m3fn(clamp(x / descale)).
+The fp8 input-pipeline recipe ("fp8blk") draws Q, K, V the same way but
+plants the outlier channels of Q and K in the same (head, channel) columns
+(one draw for Q, reused for K; then one for V), the aligned large channels of
+real query and key activations that a rotation before quantising is meant to
+spread; it then casts Q, K, V to bf16 and draws the D rotation signs (+-1,
+int8) with ``rng.integers(0, 2, D) * 2 - 1``.  The device quantises.
 
 These Gaussian tensors stand in for the captured model activations that the
 ZYFA article measures on (section "What the numbers establish, and where they
@@ -44,7 +50,7 @@ class Workload:
     Nkv: int
     D: int
     causal: bool
-    dtype: str  # "f32", "bf16" or "fp8"
+    dtype: str  # "f32", "bf16", "fp8" or "fp8blk" (bf16 inputs of the fp8 pipeline)
     value_scale: float = 1.0
     seed: int = 0
     outlier_frac: float = 0.0
@@ -101,6 +107,11 @@ WORKLOADS = {
     # key-range splitting is for; the same problem run plainly and split into
     # 8 key ranges (extra["n_splits"]; 512 work-groups, two per CU, the best
     # of 1..64 measured) merged by LSE.
+    # the fp8 input pipeline on the same problem: bf16 Q, K, V with the same
+    # outlier channels, quantised on the device with one descale per 64-row
+    # block, Q and K rotated by a signed Hadamard matrix first
+    "fp8_blocks_outlier": Workload("fp8_blocks_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8blk",
+                                   outlier_frac=0.01),
     "chunk_prefill_bf16": Workload("chunk_prefill_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16"),
     "chunk_prefill_splitkv_bf16": Workload("chunk_prefill_splitkv_bf16", 1, 32, 8, 256, 32768, 128, True, "bf16",
                                            extra={"n_splits": 8}),
@@ -134,20 +145,56 @@ def make_inputs(w: Workload):
     if w.dtype in _TORCH_DTYPE:
         dt = _TORCH_DTYPE[w.dtype]
         return tuple(torch.from_numpy(x).to(dt) for x in (q, k, v))
+    if w.dtype == "fp8blk":
+        cols = _outlier_channels(rng, q, w)
+        _outlier_channels(rng, k, w, cols, group=w.Hq // w.Hkv)
+        _outlier_channels(rng, v, w)
+        signs = (rng.integers(0, 2, size=w.D) * 2 - 1).astype(np.int8)
+        return (*(torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v)), torch.from_numpy(signs))
     if w.dtype != "fp8":
         raise ValueError(f"unknown dtype {w.dtype}")
     out, desc = [], []
     for x in (q, k, v):
-        H, D = x.shape[1], x.shape[3]
-        n_out = int(round(w.outlier_frac * H * D))
-        if n_out:
-            cols = rng.choice(H * D, size=n_out, replace=False)
-            hh, dd = np.divmod(cols, D)
-            x[:, hh, :, dd] *= w.outlier_mult
+        _outlier_channels(rng, x, w)
         code, d = quantize_e4m3(x)
         out.append(code)
         desc.append(d)
     return out[0], out[1], out[2], np.array(desc, dtype=np.float32)
+
+
+def _outlier_channels(rng, x, w, cols=None, group=1):
+    """Multiply round(outlier_frac * H * D) distinct (head, channel) columns of
+    x (B, H, N, D) by outlier_mult, in place, and return them.  Given columns
+    (drawn over the query heads) are reused, query head h mapping to head
+    h // group of x (the KV head of a GQA group); a column hit twice that way
+    is multiplied once."""
+    H, D = x.shape[1], x.shape[3]
+    if cols is None:
+        n_out = int(round(w.outlier_frac * H * D))
+        if not n_out:
+            return None
+        cols = rng.choice(H * D, size=n_out, replace=False)
+    if cols is not None and len(cols):
+        hh, dd = np.divmod(cols, D)
+        mine = np.unique((hh // group) * D + dd)
+        hh, dd = np.divmod(mine, D)
+        x[:, hh, :, dd] *= w.outlier_mult
+    return cols
+
+
+def block_descales(w, seed=1):
+    """Per-64-row-block descales for the e4m3 codes of an fp8 workload (a
+    kernel input of the block-scaled path): each tensor's per-tensor descale
+    times factors drawn uniformly from [1/2, 2] (float32), one per (batch,
+    head, block), from ``default_rng(seed)`` in the order Q, K, V.  Returns
+    three float32 numpy arrays of shape (B, H, ceil(N / 64))."""
+    _, _, _, desc = make_inputs(w)
+    rng = np.random.default_rng(seed)
+    out = []
+    for d, H, N in zip(desc, (w.Hq, w.Hkv, w.Hkv), (w.Nq, w.Nkv, w.Nkv)):
+        f = rng.uniform(0.5, 2.0, size=(w.B, H, (N + 63) // 64))
+        out.append((f * np.float64(d)).astype(np.float32))
+    return out
 
 
 def quantize_e4m3(x):

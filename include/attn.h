@@ -193,6 +193,45 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      const float* descale_q, const float* descale_k, const float* descale_v,
                      int64_t n_splits, void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/*
+ * The fp8 input pipeline (FA blog, section "FA3 — el momento Hopper": FP8
+ * with one scale per 64 x d tile and a random orthogonal Hadamard-based
+ * pre-multiplication that spreads outliers; ZYFA article, section "The ZYFA
+ * accuracy work is the sleeper contribution": a Hadamard rotation of Q and K
+ * before quantisation roughly halves the input error).
+ */
+
+/*
+ * attn_quantize_fp8 -- e4m3fn codes of a bf16 (B, H, N, D) tensor with one
+ * descale per block of 64 rows of each (batch, head) slab, optionally after
+ * rotating every row by R = diag(signs) H_D / sqrt(D) (H_D the Sylvester
+ * Hadamard matrix).  R is orthogonal, so rotating Q and K with the same
+ * signs leaves Q K^T unchanged; V is quantised without rotation.
+ *   x        : DEVICE bfloat16 (B, H, N, D), 16-byte aligned
+ *   codes    : DEVICE uint8 (B, H, N, D), 16-byte aligned
+ *   descales : DEVICE float32 (B, H, ceil(N / 64)): descale = amax / 448 of
+ *              the block (after rotation), 1 for an all-zero block
+ *   D        : 64, 128 or 256
+ *   signs    : DEVICE int8 (D) of +1 / -1, or NULL for no rotation
+ * code = nearest e4m3fn value of x * (448 / amax), ties to even, computed in
+ * float32.  One kernel on `stream`; nothing is allocated.
+ */
+int attn_quantize_fp8(const void* x, void* codes, float* descales, int64_t B, int64_t H, int64_t N, int64_t D,
+                      const int8_t* signs, attn_stream_t stream);
+
+/*
+ * attn_fwd_fp8_blocks -- attn_fwd_fp8 with one descale per 64-row block
+ * (the layout attn_quantize_fp8 writes): element i of q stands for
+ * decode(code) * dq_blocks[b, hq, i / 64], and likewise for k (dk_blocks)
+ * and v (dv_blocks), (B, Hkv, ceil(Nkv / 64)) each.  D = 64, 128 or 256;
+ * scale > 0.  Other arguments, outputs and errors as attn_fwd_fp8.
+ */
+int attn_fwd_fp8_blocks(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                        int causal, float scale,
+                        const float* dq_blocks, const float* dk_blocks, const float* dv_blocks,
+                        attn_stream_t stream);
+
 /* Static English name of a status code ("ATTN_OK", ...); never NULL. */
 const char* attn_status_string(int status);
 

@@ -154,3 +154,38 @@ def call_splitkv(n_splits=4, ws=FAKE, ws_bytes=1 << 40, **kw):
 ])
 def test_splitkv_invalid_arguments(kw):
     assert call_splitkv(**kw) == A.ATTN_ERR_INVALID_ARG
+
+
+def quant(x=FAKE, codes=FAKE, desc=FAKE, B=1, H=2, N=100, D=128, signs=None):
+    return A.lib().attn_quantize_fp8(x, codes, desc, B, H, N, D, signs, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(codes=None), dict(desc=None), dict(B=0), dict(H=0), dict(N=0), dict(D=0), dict(N=-1),
+    dict(x=FAKE + 2), dict(codes=FAKE + 8), dict(desc=FAKE + 2),
+])
+def test_quantize_invalid_arguments(kw):
+    assert quant(**kw) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("D", [32, 96, 192, 512])
+def test_quantize_unsupported_head_dim(D):
+    assert quant(D=D) == A.ATTN_ERR_UNSUPPORTED
+
+
+def blocks(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, D=128, causal=0,
+           scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE):
+    return A.lib().attn_fwd_fp8_blocks(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dq, dk, dv, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(q=None), dict(B=0), dict(Hq=3, Hkv=2),
+    dict(scale=float("nan")), dict(q=FAKE + 8),
+])
+def test_blocks_invalid_arguments(kw):
+    assert blocks(**kw) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=512), dict(D=32), dict(scale=0.0), dict(scale=-0.5)])
+def test_blocks_unsupported(kw):
+    assert blocks(**kw) == A.ATTN_ERR_UNSUPPORTED

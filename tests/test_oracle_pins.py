@@ -593,3 +593,34 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
     monkeypatch.setattr(me, "attention_head", oatt.attention_head)
     failed = [c.__name__ for c in ALL_CHECKS if not c()]
     assert failed, f"no check caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quant_pipeline_error_ordering(seed):
+    """FA blog, section "FA3 — el momento Hopper": block scales and the
+    Hadamard-based rotation each cut the fp8 error against exact attention
+    (documented there as 2.6x below per-tensor fp8 together); ZYFA article,
+    section "The ZYFA accuracy work is the sleeper contribution": the
+    rotation of Q and K about halves the input error.  On the outlier recipe
+    with Q and K outliers in shared channels, the oracle's pipeline shows both
+    steps (seeds 0-3 give 0.32-0.53x and 0.39-0.50x; 4.7-6x together).  A
+    rotation applied to Q alone, or with other signs for K, fails this."""
+    from exact_io_aware_attn_amd.inputs import Workload, make_inputs, quantize_e4m3
+    w = Workload("acc", 1, 4, 4, 512, 512, 128, False, "fp8blk", outlier_frac=0.01, seed=seed)
+    q, k, v, signs = make_inputs(w)
+    x = [t.to(torch.float64).numpy() for t in (q, k, v)]
+    ref = attention(*x, scale=w.scale)[0]
+    per_tensor = []
+    for t in x:
+        c, d = quantize_e4m3(t)
+        per_tensor.append(e4m3fn_decode(c.view(torch.uint8).numpy()) * np.float64(d))
+
+    def blocks(rotate):
+        s = signs.numpy() if rotate else None
+        return [oquant.dequantize_blocks(*oquant.quantize_blocks(t, s if i < 2 else None)) for i, t in enumerate(x)]
+
+    rmse = lambda xs: float(np.sqrt(((attention(*xs, scale=w.scale)[0] - ref) ** 2).mean()))
+    et, eb, er = rmse(per_tensor), rmse(blocks(False)), rmse(blocks(True))
+    assert eb <= 0.75 * et, (et, eb)
+    assert er <= 0.7 * eb, (eb, er)
+    assert er <= et / 2.6, (et, er)
