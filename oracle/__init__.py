@@ -19,6 +19,8 @@ keyrange       -- attention over one range of the keys (causal alignment of the
 quant          -- the fp8 input pipeline: signed Hadamard rotation of Q and K,
                   e4m3 encoding (nearest, ties to even, saturating) and
                   quantisation with one descale per 64-row block.
+backward       -- gradients dQ, dK, dV: the chain rule through the forward
+                  definition, P materialised per head.
 
 Every function cites the passage of the source pages it follows, by page title
 and section.  No function here is "parity unpinned": each one is pinned by a
@@ -30,6 +32,7 @@ from .online import online_attention_head
 from .e4m3 import e4m3fn_decode, E4M3FN_MAX
 from .keyrange import attention_range, attention_range_head, key_range_mask, merge
 from .quant import dequantize_blocks, e4m3fn_encode, hadamard, quantize_blocks, rotation
+from .backward import attention_backward, attention_backward_head, probabilities_head, row_delta
 
 __all__ = [
     "attention",
@@ -48,4 +51,8 @@ __all__ = [
     "rotation",
     "quantize_blocks",
     "dequantize_blocks",
+    "attention_backward",
+    "attention_backward_head",
+    "probabilities_head",
+    "row_delta",
 ]
