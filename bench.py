@@ -35,9 +35,12 @@ import numpy as np
 import torch
 
 from exact_io_aware_attn_amd import attn as A
-from exact_io_aware_attn_amd.inputs import WORKLOADS, make_inputs
+from exact_io_aware_attn_amd.inputs import WORKLOADS, make_grad, make_inputs
 
 METRIC = "attention fwd TFLOPS on 1 MI355X and % of dense bf16/fp8 MFMA peak"
+# the backward workload counts the five matrix products of the gradients
+# (recomputed Q K^T, dO V^T, P^T dO, dS K, dS^T Q): 2.5x the forward's flops
+METRIC_BWD = "attention bwd TFLOPS on 1 MI355X (5 matmuls counted) and % of dense bf16 MFMA peak"
 # MI355X dense MFMA peaks (TFLOP/s): bf16 2.5 PF, fp8 5.0 PF, fp32 157.3 TF.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "prefill_causal_bf16"
@@ -115,8 +118,18 @@ def copy_calibration(mib, steps):
                                            "launches": steps}}), flush=True)
 
 
+def is_bwd(w):
+    return w.extra.get("pass") == "bwd"
+
+
+def step_flops(w):
+    return float(w.flops) * (2.5 if is_bwd(w) else 1.0)
+
+
 def gpu_inputs(w, dev):
     inp = make_inputs(w)
+    if is_bwd(w):
+        inp = (*inp, make_grad(w))
     if w.dtype == "fp8blk":
         return tuple(t.to(dev) for t in inp), inp
     if w.dtype == "fp8":
@@ -140,6 +153,15 @@ def make_step(w, dev_inp, out, lse):
                 ev[1].record(stream)
         return step
 
+    if is_bwd(w):
+        # the forward outputs once, outside the timed steps; then dQ, dK, dV
+        # into buffers allocated once, with a workspace allocated once
+        q, k, v, g = dev_inp
+        A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(A.bwd_workspace_bytes(w.B, w.Hq, w.Nq), dtype=torch.uint8, device=q.device)
+        return bracket(lambda: A.bwd(q, k, v, out, lse, g, causal=w.causal, scale=w.scale, workspace=ws,
+                                     dq=dq, dk=dk, dv=dv))
     if w.dtype == "fp8blk":
         # the fp8 input pipeline: Q and K rotated and block-quantised, V
         # block-quantised, then block-scaled e4m3 attention; buffers once
@@ -212,20 +234,25 @@ def cpu_baseline(w, host_inp, n_heads, seconds):
         get_k = lambda b, h: head(k8, desc[1], b, h)
         get_v = lambda b, h: head(v8, desc[2], b, h)
     else:
-        q, k, v = host_inp
+        q, k, v = host_inp[:3]
         get_q = lambda b, h: q[b, h].to(torch.float64).numpy()
         get_k = lambda b, h: k[b, h].to(torch.float64).numpy()
         get_v = lambda b, h: v[b, h].to(torch.float64).numpy()
     done = 0
     t0 = time.perf_counter()
     for b, hq in order:
-        oracle.attention_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), w.scale, w.causal)
+        if is_bwd(w):
+            g = host_inp[3][b, hq].to(torch.float64).numpy()
+            oracle.attention_backward_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), g, w.scale,
+                                           w.causal)
+        else:
+            oracle.attention_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), w.scale, w.causal)
         done += 1
         dt = time.perf_counter() - t0
         if (n_heads and done >= n_heads) or (not n_heads and dt >= seconds):
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * w.visible_pairs * done
+    flops = 4.0 * w.D * w.visible_pairs * done * (2.5 if is_bwd(w) else 1.0)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -286,13 +313,13 @@ def main():
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
 
     ms_per_step = wall * 1e3 / args.steps
-    flops = float(w.flops)
+    flops = step_flops(w)
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_kernel_s / 1e12
     compute_dtype = "fp8" if w.dtype == "fp8blk" else w.dtype
     peak = PEAK_TFLOPS[compute_dtype]
     res = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if is_bwd(w) else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -308,6 +335,8 @@ def main():
             "workload": w.name,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
             "causal": w.causal, "scale": "1/sqrt(D)", "inputs": INPUTS.get(w.dtype, "i.i.d. N(0,1), seed 0"),
+            **({"timed": "attn_bwd: delta/lse2 prep + dK/dV + dQ launches (forward outputs computed once, "
+                         "before the timed steps); roofline over the whole backward"} if is_bwd(w) else {}),
             **({"timed": "block quantisation of Q, K (rotated) and V + block-scaled e4m3 attention; "
                          "roofline on the attention launch alone"} if w.dtype == "fp8blk" else {}),
             **({"n_splits": int(w.extra["n_splits"]),

@@ -19,7 +19,8 @@ ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/attn.h declares
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
-            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_status_string",
+            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd",
+            "attn_status_string",
             "attn_last_error", "attn_version")
 
 
@@ -61,6 +62,10 @@ def lib():
     L.attn_quantize_fp8.restype = ci
     L.attn_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
     L.attn_fwd_fp8_blocks.restype = ci
+    L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_bwd.argtypes = [vp] * 9 + [i64] * 6 + [ci, cf, ci, vp, ctypes.c_size_t, vp]
+    L.attn_bwd.restype = ci
     L.attn_status_string.argtypes = [ci]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -311,3 +316,33 @@ def fwd_fp8_blocks(q, k, v, dq_blocks, dk_blocks, dv_blocks, causal=False, scale
                                      int(causal), float(scale), dq_blocks.data_ptr(), dk_blocks.data_ptr(),
                                      dv_blocks.data_ptr(), _stream_ptr(stream)))
     return out, lse
+
+
+def bwd_workspace_bytes(B, Hq, Nq):
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """Gradients (dq, dk, dv) of bf16 attention given the forward outputs o
+    and lse (natural log) and the upstream gradient dout."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("bwd takes contiguous bfloat16 device tensors")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, int(causal),
+                          float(scale), ATTN_BF16, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_ptr(stream)))
+    return dq, dk, dv

@@ -232,6 +232,68 @@ int attn_fwd_fp8_blocks(const void* q, const void* k, const void* v, void* o, fl
                      dv_blocks, nullptr, stream, true);
 }
 
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq) {
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  const int64_t one = (B * Hq * Nq * 4 + 255) / 256 * 256;
+  return (size_t)(2 * one);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+             int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL device pointers");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  for (const void* t : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(t)) return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device buffer of at least %zu bytes",
+                need);
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "the backward pass takes bf16 only (dtype=%d)", dtype);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the backward pass takes D = 64 or 128", (long long)D);
+  const int64_t lim = (int64_t)1 << 31;
+  if (Nq * D * 2 >= lim || Nkv * D * 2 >= lim)
+    return fail(ATTN_ERR_UNSUPPORTED, "a (batch, head) slab reaches 2^31 bytes");
+  if (B * Hq * Nq >= lim || B * Hq > (int64_t)INT32_MAX)
+    return fail(ATTN_ERR_UNSUPPORTED, "B*Hq*Nq must be < 2^31");
+  attn::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const size_t one = need / 2;
+  p.delta = static_cast<float*>(workspace);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + one);
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Nq = (int)Nq;
+  p.Nkv = (int)Nkv;
+  p.D = (int)D;
+  p.group = (int)(Hq / Hkv);
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  hipError_t err = attn::launch_bwd(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
 size_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D, int64_t n_splits) {
   if (B < 1 || Hq < 1 || Nq < 1 || D < 1 || n_splits < 1) return 0;
   const int64_t rows = B * Hq * Nq;

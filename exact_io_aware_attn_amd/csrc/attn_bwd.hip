@@ -1,0 +1,476 @@
+// attn_bwd.hip -- exact attention backward on gfx950 (bf16, D = 64 and 128).
+//
+// FlashAttention summary page, method paragraph: the backward pass recomputes
+// S = Q K^T instead of storing it; FlashAttention v1/v2/v3/v4 blog post,
+// section "FA1 — el cambio de orden de las operaciones": only the softmax
+// statistics are kept, and S is recomputed block by block from Q, K and
+// them.  With the natural-log LSE of the forward pass, P = exp(scale S - LSE)
+// needs no running max, and the gradients of the forward definition are
+//   dV = P^T dO,  dP = dO V^T,  delta_i = dO_i . O_i (= sum_j P_ij dP_ij),
+//   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,
+// with dK and dV of a KV head summed over the query heads of its group.
+//
+// Three launches on one stream:
+//   * prep: delta_i = dO_i . O_i in float32 and lse2_i = LSE_i log2(e)
+//     (+inf for a row that saw no key, so that its P is 0), into a
+//     caller-owned workspace;
+//   * dK/dV: one work-group per (batch, KV head, 128 keys), 32 keys per wave
+//     held in registers with the wave's dK^T and dV^T accumulators; Q and dO
+//     tiles of 64 rows of every query head of the group stream through LDS.
+//     S = Q K^T and dP = dO V^T put one key per lane (column) and 16 query
+//     rows per lane in the accumulator registers, which rounded to bf16 are
+//     the B operands of dV^T += dO^T P and dK^T += Q^T dS as they stand; the
+//     A operands dO^T and Q^T come from the transposing LDS read.  No
+//     atomics: each key's gradients are owned by one wave.
+//   * dQ: one work-group per (batch, query head, 128 rows), the forward
+//     pass's layout: Q and dO rows in registers (one query per lane), K and V
+//     tiles of 64 keys in LDS; S^T = K Q^T, dP^T = V dO^T, then
+//     dQ^T += K^T dS^T with K^T from the transposing read.
+// S and dP are recomputed in both the dK/dV and the dQ launch (seven matrix
+// products where five would do with atomic dQ accumulation): the results
+// are deterministic.
+//
+// Tiles are staged global -> registers -> LDS one tile ahead.  Their rows are
+// read both as row fragments (16 rows of one 16-byte chunk per LDS phase)
+// and through ds_read_b64_tr_b16 (4 rows x 4 chunks per phase); the XOR
+// swizzle rt_swz keeps both conflict-free at D = 128.
+#include "attn_common.h"
+#include "attn_dma.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Chunk swizzle for rows read both ways.  D = 128 (16 chunks): row reads
+// put rows 0..15 in a phase, and 4 (row & 3) + ((row >> 2) & 3) is a
+// permutation of 0..15 over them; transposing reads put rows 4g..4g+3 and
+// chunks 4c..4c+3 in a phase, where the term 4 (row & 3) sends each row to
+// its own group of four chunks.  D = 64 (8 chunks, two rows per 256 bytes):
+// m = (row >> 1) & 7 separates the rows of one parity; m ^ 4 (m & 1) gives
+// rows 4g and 4g + 2 different halves of the 8 chunks.
+template <int D>
+__device__ __forceinline__ int rt_swz(int row) {
+  if constexpr (D % 128 == 0) {
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  } else {
+    const int m = (row >> 1) & 7;
+    return m ^ ((m & 1) << 2);
+  }
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// A operand fragment from rows of an LDS tile: row `row`, chunk `ch`.
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const char* tile, int row, int ch) {
+  return lds_load16(tile, (uint32_t)(row * (2 * D) + ((ch ^ rt_swz<D>(row)) << 4)));
+}
+
+// A operand fragment of X^T (m = d, k = rows) for the 32 columns of d-block
+// db and the 16 rows starting at r0: lane l gets column 32 db + l % 32 at
+// rows r0 + 4h + 0..3 and r0 + 8 + 4h + 0..3 (h = l / 32).
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int db, int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15, h = lane >> 5;
+  const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int rlo = r0 + 4 * h + (r16 >> 2), rhi = rlo + 8;
+  const uint32_t alo = (uint32_t)(rlo * (2 * D) + ((chunk ^ rt_swz<D>(rlo)) << 4) + ((r16 & 1) << 3));
+  const uint32_t ahi = (uint32_t)(rhi * (2 * D) + ((chunk ^ rt_swz<D>(rhi)) << 4) + ((r16 & 1) << 3));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + alo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + ahi));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
+// ---- prep: delta = rowsum(dO * O), lse2 = LSE log2(e) ---------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;       // lanes per row, 16 bytes each
+  constexpr int RPB = 256 / LPR;   // rows per work-group
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>((const __bf16*)p.o + row * D + sub * 8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>((const __bf16*)p.dout + row * D + sub * 8);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc += bf_lo(aw[j]) * bf_lo(gw[j]) + bf_hi(aw[j]) * bf_hi(gw[j]);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (sub == 0 && row < rows) {
+    p.delta[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---- dK, dV ---------------------------------------------------------------------------
+
+template <int D>
+struct KVCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 32 * NW;             // keys per work-group
+  static constexpr int BQ = 64;                  // query rows per LDS tile
+  static constexpr int RP = 2 * D;               // bf16 row pitch (bytes)
+  static constexpr int CH = RP / 16;             // 16-byte chunks per row
+  static constexpr int NC = D / 16;              // 16-wide d chunks (S, dP contraction)
+  static constexpr int NDB = D / 32;             // 32-row blocks of dK^T, dV^T
+  static constexpr int TILE = BQ * RP;           // bytes of one Q or dO tile
+  static constexpr int LD = 2 * TILE / 16 / NT;  // 16-byte loads per thread per tile pair
+  static constexpr int LDS = 2 * TILE + 2 * BQ * 4;
+  static_assert((2 * TILE / 16) % NT == 0, "tiles must split evenly over the threads");
+  static_assert(2 * BQ <= NT, "one thread per lse2 / delta value");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using C = KVCfg<D>;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  char* const ldsQ = lds;
+  char* const ldsO = lds + C::TILE;
+  float* const ldsL = reinterpret_cast<float*>(lds + 2 * C::TILE);
+  float* const ldsD = ldsL + C::BQ;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  // work decomposition: causal runs the key tiles with the most query rows
+  // (smallest k0) first
+  const int n_kt = (p.Nkv + C::BK - 1) / C::BK;
+  const int BH = p.B * p.Hkv;
+  const int wg = xcd_remap(blockIdx.x, n_kt * BH);
+  const int kt = p.causal ? wg / BH : wg % n_kt;
+  const int bh = p.causal ? wg % BH : wg / n_kt;
+  const int hk = bh % p.Hkv;
+  const int b = bh / p.Hkv;
+  const int k0 = kt * C::BK;
+  const int k0w = k0 + 32 * wave;
+  const int key = k0w + l32;
+
+  // this wave's K and V rows in B-operand layout (d chunk 2c + h)
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  u32x4 kreg[C::NC], vreg[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) {
+    kreg[c] = buf_load16(rk, (uint32_t)(key * C::RP + (2 * c + h) * 16));
+    vreg[c] = buf_load16(rv, (uint32_t)(key * C::RP + (2 * c + h) * 16));
+  }
+
+  f32x16 adv[C::NDB], adk[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    adv[db] = f32x16{};
+    adk[db] = f32x16{};
+  }
+
+  // query tiles: every head of the group, from the first tile with a row
+  // that sees key k0
+  const int kv_off = p.Nkv - p.Nq;
+  const int n_qt = (p.Nq + C::BQ - 1) / C::BQ;
+  const int qt0 = p.causal ? min(max(0, k0 - kv_off) / C::BQ, n_qt) : 0;
+  const int nq = n_qt - qt0;
+  const int T = p.group * nq;
+  const float c = p.scale * kLog2e;
+
+  // staging registers for one tile (Q and dO rows, lse2, delta)
+  u32x4 st[C::LD];
+  float st_l = 0.0f;
+  auto stage = [&](int t) {
+    const int hq = hk * p.group + t / nq;
+    const int q0 = (qt0 + t % nq) * C::BQ;
+    const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab * D, (uint32_t)(p.Nq * C::RP));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const __bf16*)p.dout + q_slab * D, (uint32_t)(p.Nq * C::RP));
+#pragma unroll
+    for (int i = 0; i < C::LD; ++i) {
+      const int u = tid + i * C::NT;
+      const int which = u / (C::BQ * C::CH);
+      const int rem = u % (C::BQ * C::CH);
+      const uint32_t off = (uint32_t)((q0 + rem / C::CH) * C::RP + (rem % C::CH) * 16);
+      st[i] = which == 0 ? buf_load16(rq, off) : buf_load16(ro, off);
+    }
+    if (tid < 2 * C::BQ) {
+      const int r = q0 + (tid % C::BQ);
+      const bool live = r < p.Nq;
+      st_l = tid < C::BQ ? (live ? p.lse2[q_slab + r] : INFINITY) : (live ? p.delta[q_slab + r] : 0.0f);
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::LD; ++i) {
+      const int u = tid + i * C::NT;
+      const int which = u / (C::BQ * C::CH);
+      const int rem = u % (C::BQ * C::CH);
+      const int row = rem / C::CH, ch = rem % C::CH;
+      lds_store16(which == 0 ? ldsQ : ldsO, (uint32_t)(row * C::RP + ((ch ^ rt_swz<D>(row)) << 4)), st[i]);
+    }
+    if (tid < 2 * C::BQ) ldsL[tid] = st_l;  // ldsD follows ldsL
+  };
+
+  if (T > 0) stage(0);
+  for (int t = 0; t < T; ++t) {
+    const int q0 = (qt0 + t % nq) * C::BQ;
+    __syncthreads();  // the previous tile's LDS reads are done
+    commit();
+    __syncthreads();
+    if (t + 1 < T) stage(t + 1);
+
+#pragma unroll
+    for (int qb = 0; qb < C::BQ / 32; ++qb) {
+      const int r0 = q0 + 32 * qb;  // first query row of the block
+      // wave-uniform skips: rows past Nq, or every row above this wave's keys
+      if (r0 >= p.Nq) continue;
+      if (p.causal && r0 + 31 + kv_off < k0w) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NC; ++cc) {
+        s = mfma_bf16(row_frag<D>(ldsQ, 32 * qb + l32, 2 * cc + h), kreg[cc], s);
+        dp = mfma_bf16(row_frag<D>(ldsO, 32 * qb + l32, 2 * cc + h), vreg[cc], dp);
+      }
+      // lse2 and delta of this lane's 16 rows: 32 qb + 8 j + 4 h + 0..3
+      float L[16], Dl[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldsL + 32 * qb + 8 * j + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ldsD + 32 * qb + 8 * j + 4 * h);
+        L[4 * j + 0] = l4.x; L[4 * j + 1] = l4.y; L[4 * j + 2] = l4.z; L[4 * j + 3] = l4.w;
+        Dl[4 * j + 0] = d4.x; Dl[4 * j + 1] = d4.y; Dl[4 * j + 2] = d4.z; Dl[4 * j + 3] = d4.w;
+      }
+      const bool mask = p.causal && r0 + kv_off < k0w + 31;
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = exp2_fast(__builtin_fmaf(s[r], c, -L[r]));
+        if (mask && key > r0 + 8 * (r / 4) + 4 * h + (r % 4) + kv_off) e = 0.0f;
+        pv[r] = e;
+        dsv[r] = e * (dp[r] - Dl[r]);
+      }
+      u32x4 pf[2], df[2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        pf[kc] = u32x4{pack_bf16x2(pv[8 * kc + 0], pv[8 * kc + 1]), pack_bf16x2(pv[8 * kc + 2], pv[8 * kc + 3]),
+                       pack_bf16x2(pv[8 * kc + 4], pv[8 * kc + 5]), pack_bf16x2(pv[8 * kc + 6], pv[8 * kc + 7])};
+        df[kc] = u32x4{pack_bf16x2(dsv[8 * kc + 0], dsv[8 * kc + 1]), pack_bf16x2(dsv[8 * kc + 2], dsv[8 * kc + 3]),
+                       pack_bf16x2(dsv[8 * kc + 4], dsv[8 * kc + 5]), pack_bf16x2(dsv[8 * kc + 6], dsv[8 * kc + 7])};
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          adv[db] = mfma_bf16(tr_frag<D>(ldsO, 32 * qb + 16 * kc, db, lane), pf[kc], adv[db]);
+          adk[db] = mfma_bf16(tr_frag<D>(ldsQ, 32 * qb + 16 * kc, db, lane), df[kc], adk[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: lane = key, registers = d ----------------------------------------
+  if (key < p.Nkv) {
+    const int64_t row = kv_slab + (int64_t)key * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * h;
+        store_o4(p.dv, false, row + d, adv[db][4 * g + 0], adv[db][4 * g + 1], adv[db][4 * g + 2],
+                 adv[db][4 * g + 3]);
+        store_o4(p.dk, false, row + d, adk[db][4 * g + 0] * p.scale, adk[db][4 * g + 1] * p.scale,
+                 adk[db][4 * g + 2] * p.scale, adk[db][4 * g + 3] * p.scale);
+      }
+    }
+  }
+}
+
+// ---- dQ -------------------------------------------------------------------------------
+
+template <int D>
+struct QCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = 32 * NW;             // query rows per work-group
+  static constexpr int BC = 64;                  // keys per LDS tile
+  static constexpr int RP = 2 * D;
+  static constexpr int CH = RP / 16;
+  static constexpr int NC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int TILE = BC * RP;
+  static constexpr int LD = 2 * TILE / 16 / NT;
+  static constexpr int LDS = 2 * TILE;
+  static_assert((2 * TILE / 16) % NT == 0, "tiles must split evenly over the threads");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  char* const ldsK = lds;
+  char* const ldsV = lds + C::TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int n_qt = (p.Nq + C::BR - 1) / C::BR;
+  const int wg = xcd_remap(blockIdx.x, n_qt * p.B * p.Hq);
+  const int qt_raw = wg % n_qt;
+  const int bh = wg / n_qt;
+  const int hq = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int qt = p.causal ? n_qt - 1 - qt_raw : qt_raw;
+  const int hk = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int q0w = q0 + 32 * wave;
+  const int qrow = q0w + l32;
+
+  const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab * D, (uint32_t)(p.Nq * C::RP));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const __bf16*)p.dout + q_slab * D, (uint32_t)(p.Nq * C::RP));
+  u32x4 qreg[C::NC], oreg[C::NC];
+#pragma unroll
+  for (int cc = 0; cc < C::NC; ++cc) {
+    qreg[cc] = buf_load16(rq, (uint32_t)(qrow * C::RP + (2 * cc + h) * 16));
+    oreg[cc] = buf_load16(ro, (uint32_t)(qrow * C::RP + (2 * cc + h) * 16));
+  }
+  const bool live = qrow < p.Nq;
+  const float lq = live ? p.lse2[q_slab + qrow] : INFINITY;
+  const float dq_row = live ? p.delta[q_slab + qrow] : 0.0f;
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+
+  const int kv_off = p.Nkv - p.Nq;
+  int kv_end = p.Nkv;
+  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + kv_off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
+  const int klim = p.causal ? min(p.Nkv - 1, qrow + kv_off) : p.Nkv - 1;  // last visible key
+  const float c = p.scale * kLog2e;
+
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  u32x4 st[C::LD];
+  auto stage = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::LD; ++i) {
+      const int u = tid + i * C::NT;
+      const int which = u / (C::BC * C::CH);
+      const int rem = u % (C::BC * C::CH);
+      const uint32_t off = (uint32_t)((kt * C::BC + rem / C::CH) * C::RP + (rem % C::CH) * 16);
+      st[i] = which == 0 ? buf_load16(rk, off) : buf_load16(rv, off);
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::LD; ++i) {
+      const int u = tid + i * C::NT;
+      const int which = u / (C::BC * C::CH);
+      const int rem = u % (C::BC * C::CH);
+      const int row = rem / C::CH, ch = rem % C::CH;
+      lds_store16(which == 0 ? ldsK : ldsV, (uint32_t)(row * C::RP + ((ch ^ rt_swz<D>(row)) << 4)), st[i]);
+    }
+  };
+
+  if (n_kt > 0) stage(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    commit();
+    __syncthreads();
+    if (kt + 1 < n_kt) stage(kt + 1);
+    const int key0 = kt * C::BC;
+    // wave-uniform: this wave's rows see none of the tile
+    if (p.causal && key0 > q0w + 31 + kv_off) continue;
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NC; ++cc) {
+        s[kb] = mfma_bf16(row_frag<D>(ldsK, 32 * kb + l32, 2 * cc + h), qreg[cc], s[kb]);
+        dp[kb] = mfma_bf16(row_frag<D>(ldsV, 32 * kb + l32, 2 * cc + h), oreg[cc], dp[kb]);
+      }
+    }
+    const bool mask = key0 + C::BC - 1 > klim || key0 + C::BC > p.Nkv;
+    u32x4 df[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
+        if (mask && key0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
+        dsv[r] = e * (dp[kb][r] - dq_row);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        df[2 * kb + kc] = u32x4{pack_bf16x2(dsv[8 * kc + 0], dsv[8 * kc + 1]), pack_bf16x2(dsv[8 * kc + 2], dsv[8 * kc + 3]),
+                                pack_bf16x2(dsv[8 * kc + 4], dsv[8 * kc + 5]), pack_bf16x2(dsv[8 * kc + 6], dsv[8 * kc + 7])};
+    }
+#pragma unroll
+    for (int s16 = 0; s16 < 4; ++s16) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) acc[db] = mfma_bf16(tr_frag<D>(ldsK, 16 * s16, db, lane), df[s16], acc[db]);
+    }
+  }
+
+  if (live) {
+    const int64_t row = (q_slab + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * h;
+        store_o4(p.dq, false, row + d, acc[db][4 * g + 0] * p.scale, acc[db][4 * g + 1] * p.scale,
+                 acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch(const BwdParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  const int64_t prep_wg = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+  const int64_t kv_wg = (int64_t)((p.Nkv + KVCfg<D>::BK - 1) / KVCfg<D>::BK) * p.B * p.Hkv;
+  const int64_t q_wg = (int64_t)((p.Nq + QCfg<D>::BR - 1) / QCfg<D>::BR) * p.B * p.Hq;
+  if (prep_wg >= ((int64_t)1 << 31) || kv_wg >= ((int64_t)1 << 31) || q_wg >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)prep_wg), dim3(256), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)q_wg), dim3(QCfg<D>::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  switch (p.D) {
+    case 64: return launch<64>(p, stream);
+    case 128: return launch<128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

@@ -101,6 +101,10 @@ WORKLOADS = {
     },
     # fp8 e4m3 diffusion-style attention with 1% outlier channels
     "fp8_outlier": Workload("fp8_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01),
+    # the backward pass of the causal prefill problem (extra["pass"]): dQ, dK,
+    # dV from Q, K, V, the forward O and LSE and an upstream dO
+    "bwd_causal_bf16": Workload("bwd_causal_bf16", 4, 32, 32, 4096, 4096, 128, True, "bf16",
+                                extra={"pass": "bwd"}),
     # chunked prefill: a 256-token chunk against a 32K-token context, GQA,
     # causal (bottom-right: the chunk sees the whole context and itself
     # causally).  B * Hq * query tiles = 64 work-groups for 256 CUs, the case
@@ -203,6 +207,14 @@ def quantize_e4m3(x):
     descale = np.float32(amax / E4M3FN_MAX) if amax > 0 else np.float32(1.0)
     y = np.clip(x / np.float64(descale), -E4M3FN_MAX, E4M3FN_MAX)
     return torch.from_numpy(y).to(torch.float8_e4m3fn), descale
+
+
+def make_grad(w: Workload, seed_offset=1000):
+    """Upstream gradient dO of the backward pass: standard normal, shape
+    (B, Hq, Nq, D), from ``default_rng(w.seed + seed_offset)``, cast to bf16."""
+    rng = np.random.default_rng(w.seed + seed_offset)
+    g = rng.standard_normal((w.B, w.Hq, w.Nq, w.D))
+    return torch.from_numpy(g).to(torch.bfloat16)
 
 
 def random_problem(B, Hq, Hkv, Nq, Nkv, D, dtype="bf16", seed=0, value_scale=1.0, causal=False):

@@ -232,6 +232,45 @@ int attn_fwd_fp8_blocks(const void* q, const void* k, const void* v, void* o, fl
                         const float* dq_blocks, const float* dk_blocks, const float* dv_blocks,
                         attn_stream_t stream);
 
+/*
+ * The backward pass (FlashAttention summary page, method paragraph: the
+ * backward pass recomputes S = Q K^T rather than storing it; blog post
+ * "FlashAttention v1/v2/v3/v4", section "FA1 — el cambio de orden de las
+ * operaciones": only the softmax statistics are kept; FFPA README feature
+ * table: forward and backward).
+ */
+
+/* Bytes of workspace attn_bwd needs: two float32 (B, Hq, Nq) arrays, each
+ * rounded up to 256 bytes.  0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq);
+
+/*
+ * attn_bwd -- gradients of O = softmax(scale Q K^T + mask) V with respect to
+ * Q, K and V, given the upstream gradient dO:
+ *   P = exp(scale Q K^T - LSE) (masked),  dV = P^T dO,  dP = dO V^T,
+ *   delta_i = dO_i . O_i,  dS = P * (dP - delta),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV of a KV head summed over the query heads of its group.
+ *   q, o, dout, dq : DEVICE bf16 (B, Hq, Nq, D)
+ *   k, v, dk, dv   : DEVICE bf16 (B, Hkv, Nkv, D)
+ *   lse            : DEVICE float32 (B, Hq, Nq), natural log, as attn_fwd
+ *                    writes it (-inf for a row that sees no key)
+ *   o, lse         : the forward outputs for the same q, k, v, causal, scale
+ *   workspace      : DEVICE, 16-byte aligned, >= attn_bwd_workspace_bytes;
+ *                    overwritten (the library allocates nothing)
+ *   dtype          : ATTN_BF16 only; D = 64 or 128; causal and scale as
+ *                    attn_fwd (any finite scale).
+ * Outputs are overwritten (not accumulated into).  float32 accumulation;
+ * every key's dK/dV and every row's dQ is computed by one wave, without
+ * atomics, so results are deterministic.  Three kernels on `stream`.
+ * Errors: ATTN_ERR_INVALID_ARG (NULL, sizes, alignment, workspace size),
+ * ATTN_ERR_UNSUPPORTED (dtype, D, sizes past 2^31), ATTN_ERR_HIP.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
+             int64_t D, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+             attn_stream_t stream);
+
 /* Static English name of a status code ("ATTN_OK", ...); never NULL. */
 const char* attn_status_string(int status);
 

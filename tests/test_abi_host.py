@@ -189,3 +189,28 @@ def test_blocks_invalid_arguments(kw):
 @pytest.mark.parametrize("kw", [dict(D=96), dict(D=512), dict(D=32), dict(scale=0.0), dict(scale=-0.5)])
 def test_blocks_unsupported(kw):
     assert blocks(**kw) == A.ATTN_ERR_UNSUPPORTED
+
+
+def bwd_call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=2, Hkv=2,
+             Nq=64, Nkv=64, D=128, causal=0, scale=0.1, dtype=A.ATTN_BF16, ws=FAKE, ws_bytes=1 << 20):
+    return A.lib().attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, ws,
+                            ws_bytes, None)
+
+
+def test_bwd_workspace_size():
+    assert A.bwd_workspace_bytes(2, 3, 100) == 2 * ((2 * 3 * 100 * 4 + 255) // 256 * 256)
+    assert A.bwd_workspace_bytes(0, 3, 100) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(lse=None), dict(do=None), dict(dq=None), dict(dk=None), dict(dv=None), dict(ws=None),
+    dict(ws_bytes=16), dict(B=0), dict(Hq=3, Hkv=2), dict(scale=float("nan")), dict(dtype=9), dict(q=FAKE + 8),
+    dict(lse=FAKE + 2), dict(ws=FAKE + 4),
+])
+def test_bwd_invalid_arguments(kw):
+    assert bwd_call(**kw) == A.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(dtype=A.ATTN_F32), dict(dtype=A.ATTN_FP8_E4M3)])
+def test_bwd_unsupported(kw):
+    assert bwd_call(**kw) == A.ATTN_ERR_UNSUPPORTED

@@ -1,0 +1,127 @@
+"""GPU parity of the backward pass (attn_bwd through the C ABI) against the
+oracle's gradients (``oracle.attention_backward``, the chain rule through
+the forward definition in float64).
+
+Inputs: Q, K, V of the bf16 recipe and dO standard normal in bf16
+(``inputs.make_grad``); O and LSE come from the library's own forward pass,
+as a training step would pass them.
+
+Tolerance (the pages state none for gradients; derived from the arithmetic):
+the kernels round P and dS to bf16 (relative 2^-9) before the products, and
+delta = dO . O uses the bf16 forward output; every product accumulates in
+float32.  The bound is 2e-2 of each gradient's largest magnitude, about ten
+bf16 roundings of the largest term, checked element by element over dQ, dK
+and dV; rows that see no key must have dQ exactly 0.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_attn_amd import attn as A
+from exact_io_aware_attn_amd.inputs import WORKLOADS, Workload, make_grad, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def run_bwd(w):
+    q, k, v = make_inputs(w)
+    g = make_grad(w)
+    dev = [t.cuda() for t in (q, k, v, g)]
+    O, L = A.fwd(dev[0], dev[1], dev[2], causal=w.causal, scale=w.scale)
+    dq, dk, dv = A.bwd(dev[0], dev[1], dev[2], O, L, dev[3], causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return (q, k, v, g), tuple(t.float().cpu().numpy() for t in (dq, dk, dv))
+
+
+def rel_err(x, ref):
+    return float(np.abs(x - ref).max()) / max(float(np.abs(ref).max()), 1e-30)
+
+
+CASES = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal)
+    (1, 2, 2, 200, 300, 128, True),       # ragged, causal with Nq < Nkv
+    (2, 4, 2, 130, 257, 64, False),       # GQA, ragged key tile
+    (1, 2, 1, 333, 129, 128, True),       # Nq > Nkv: the first rows see no key
+    (1, 2, 2, 1, 70, 128, True),          # one query row
+    (1, 3, 1, 65, 65, 64, True),          # MQA
+    (1, 2, 2, 257, 1000, 128, False),     # cross attention, several key work-groups
+    (1, 2, 2, 64, 64, 128, False),        # exactly one tile
+    (1, 4, 4, 513, 513, 128, True),       # several query and key tiles on the diagonal
+    (1, 2, 2, 300, 1, 64, True),          # one key
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_parity(case):
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    note(f"bwd {case}")
+    w = Workload("bwd", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", seed=3)
+    (q, k, v, g), (dq, dk, dv) = run_bwd(w)
+    ref = oracle.attention_backward(*(t.to(torch.float64).numpy() for t in (q, k, v, g)), scale=w.scale,
+                                    causal=causal)
+    for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert np.isfinite(x).all(), f"{name}: non-finite values"
+        e = rel_err(x, r)
+        note(f"  {name}: max |err| / max |ref| = {e:.3e}")
+        assert e <= TOL, f"{name}: {e:.3e} > {TOL}"
+    seen = oracle.visible_mask(Nq, Nkv, causal).any(axis=1)
+    assert (dq[:, :, ~seen] == 0).all(), "rows without keys must get dQ = 0"
+
+
+def test_bwd_deterministic():
+    w = Workload("bwd_det", 1, 4, 2, 300, 300, 128, True, "bf16", seed=5)
+    q, k, v = (t.cuda() for t in make_inputs(w))
+    g = make_grad(w).cuda()
+    O, L = A.fwd(q, k, v, causal=True, scale=w.scale)
+    first = A.bwd(q, k, v, O, L, g, causal=True, scale=w.scale)
+    second = A.bwd(q, k, v, O, L, g, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bwd_scale_variants():
+    """Scale 0 (uniform P: dQ = dK = 0) and a negative scale."""
+    w = Workload("bwd_sc", 1, 2, 2, 150, 170, 64, True, "bf16", seed=7)
+    q, k, v = make_inputs(w)
+    g = make_grad(w)
+    dev = [t.cuda() for t in (q, k, v, g)]
+    for sc in (0.0, -0.11):
+        note(f"bwd scale={sc}")
+        O, L = A.fwd(dev[0], dev[1], dev[2], causal=True, scale=sc)
+        dq, dk, dv = A.bwd(dev[0], dev[1], dev[2], O, L, dev[3], causal=True, scale=sc)
+        torch.cuda.synchronize()
+        ref = oracle.attention_backward(*(t.to(torch.float64).numpy() for t in (q, k, v, g)), scale=sc, causal=True)
+        for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            x = x.float().cpu().numpy()
+            if np.abs(r).max() == 0:
+                assert (x == 0).all(), name
+            else:
+                assert rel_err(x, r) <= TOL, (sc, name, rel_err(x, r))
+
+
+def test_bwd_full_size_sampled():
+    """The benchmarked problem (B4 H32 N4096 D128, causal): every gradient of
+    three sampled heads against the oracle's per-head gradients."""
+    w = WORKLOADS["prefill_causal_bf16"]
+    note(f"{w.name} backward, full size")
+    (q, k, v, g), (dq, dk, dv) = run_bwd(w)
+    rng = np.random.default_rng(2)
+    heads = [(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))]
+    worst = 0.0
+    for b, h in heads:
+        r_q, r_k, r_v = oracle.attention_backward_head(
+            *(t[b, h].to(torch.float64).numpy() for t in (q, k, v, g)), scale=w.scale, causal=w.causal)
+        for x, r in ((dq[b, h], r_q), (dk[b, h], r_k), (dv[b, h], r_v)):
+            worst = max(worst, rel_err(x, r))
+    note(f"{w.name}: worst max |err| / max |ref| over 3 heads = {worst:.3e}")
+    assert worst <= TOL
