@@ -30,10 +30,13 @@
 // products where five would do with atomic dQ accumulation): the results
 // are deterministic.
 //
-// Tiles are staged global -> registers -> LDS one tile ahead.  Their rows are
-// read both as row fragments (16 rows of one 16-byte chunk per LDS phase)
-// and through ds_read_b64_tr_b16 (4 rows x 4 chunks per phase); the XOR
-// swizzle rt_swz keeps both conflict-free at D = 128.
+// Q/dO and K/V tiles stream into LDS with direct-to-LDS buffer loads, two
+// slots, one barrier per tile (the next tile's loads are issued right after
+// it).  Their rows are read both as row fragments (16 rows of one 16-byte
+// chunk per LDS phase) and through ds_read_b64_tr_b16 (4 rows x 4 chunks per
+// phase); the XOR swizzle rt_swz keeps both conflict-free at D = 128.  The
+// dK/dV kernel runs one wave per SIMD (its accumulators take 2 D registers
+// per lane); the dQ kernel runs two.
 #include "attn_common.h"
 #include "attn_dma.h"
 #include "attn_launch.h"
@@ -63,28 +66,6 @@ __device__ __forceinline__ int rt_swz(int row) {
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-// A operand fragment from rows of an LDS tile: row `row`, chunk `ch`.
-template <int D>
-__device__ __forceinline__ u32x4 row_frag(const char* tile, int row, int ch) {
-  return lds_load16(tile, (uint32_t)(row * (2 * D) + ((ch ^ rt_swz<D>(row)) << 4)));
-}
-
-// A operand fragment of X^T (m = d, k = rows) for the 32 columns of d-block
-// db and the 16 rows starting at r0: lane l gets column 32 db + l % 32 at
-// rows r0 + 4h + 0..3 and r0 + 8 + 4h + 0..3 (h = l / 32).
-template <int D>
-__device__ __forceinline__ u32x4 tr_frag(const char* tile, int r0, int db, int lane) {
-  const int g16 = lane >> 4, r16 = lane & 15, h = lane >> 5;
-  const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
-  const int rlo = r0 + 4 * h + (r16 >> 2), rhi = rlo + 8;
-  const uint32_t alo = (uint32_t)(rlo * (2 * D) + ((chunk ^ rt_swz<D>(rlo)) << 4) + ((r16 & 1) << 3));
-  const uint32_t ahi = (uint32_t)(rhi * (2 * D) + ((chunk ^ rt_swz<D>(rhi)) << 4) + ((r16 & 1) << 3));
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + alo));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + ahi));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2.x, l2.y, h2.x, h2.y};
-}
 
 // ---- prep: delta = rowsum(dO * O), lse2 = LSE log2(e) ---------------------------------
 
@@ -121,38 +102,36 @@ struct KVCfg {
   static constexpr int BK = 32 * NW;             // keys per work-group
   static constexpr int BQ = 64;                  // query rows per LDS tile
   static constexpr int RP = 2 * D;               // bf16 row pitch (bytes)
-  static constexpr int CH = RP / 16;             // 16-byte chunks per row
   static constexpr int NC = D / 16;              // 16-wide d chunks (S, dP contraction)
   static constexpr int NDB = D / 32;             // 32-row blocks of dK^T, dV^T
   static constexpr int TILE = BQ * RP;           // bytes of one Q or dO tile
-  static constexpr int LD = 2 * TILE / 16 / NT;  // 16-byte loads per thread per tile pair
-  static constexpr int LDS = 2 * TILE + 2 * BQ * 4;
-  static_assert((2 * TILE / 16) % NT == 0, "tiles must split evenly over the threads");
+  static constexpr int DMA = TILE / 1024 / NW;   // direct-to-LDS loads per wave per tile
+  static constexpr int SLOT = 2 * TILE + 2 * BQ * 4;  // Q, dO, lse2, delta
+  static constexpr int LDS = 2 * SLOT;           // two slots
+  static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
   static_assert(2 * BQ <= NT, "one thread per lse2 / delta value");
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using C = KVCfg<D>;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-  char* const ldsQ = lds;
-  char* const ldsO = lds + C::TILE;
-  float* const ldsL = reinterpret_cast<float*>(lds + 2 * C::TILE);
-  float* const ldsD = ldsL + C::BQ;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const int g16 = lane >> 4, r16 = lane & 15;
 
-  // work decomposition: causal runs the key tiles with the most query rows
-  // (smallest k0) first
+  // work decomposition: the key tiles of one (batch, KV head) are
+  // neighbours, so they run together on one XCD and share its Q/dO in L2
   const int n_kt = (p.Nkv + C::BK - 1) / C::BK;
-  const int BH = p.B * p.Hkv;
-  const int wg = xcd_remap(blockIdx.x, n_kt * BH);
-  const int kt = p.causal ? wg / BH : wg % n_kt;
-  const int bh = p.causal ? wg % BH : wg / n_kt;
+  const int wg = xcd_remap(blockIdx.x, n_kt * p.B * p.Hkv);
+  const int kt = wg % n_kt;
+  const int bh = wg / n_kt;
   const int hk = bh % p.Hkv;
   const int b = bh / p.Hkv;
   const int k0 = kt * C::BK;
@@ -177,6 +156,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     adk[db] = f32x16{};
   }
 
+  // per-lane LDS offsets: row fragments (row l32, chunk 2c + h) and
+  // transposing reads (rows 4h + r16/4 and +8, chunk 4db + ...); a block or
+  // row offset that is a multiple of 16 rows leaves the swizzle unchanged
+  uint32_t rf[C::NC], tl[C::NDB], th[C::NDB];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) rf[c] = (uint32_t)(l32 * C::RP + (((2 * c + h) ^ rt_swz<D>(l32)) << 4));
+  {
+    const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+      tl[db] = (uint32_t)(rlo * C::RP + ((chunk ^ rt_swz<D>(rlo)) << 4) + ((r16 & 1) << 3));
+      th[db] = (uint32_t)(rhi * C::RP + ((chunk ^ rt_swz<D>(rhi)) << 4) + ((r16 & 1) << 3));
+    }
+  }
+  auto trf = [&](const char* tile, int r0, int db) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + r0 * C::RP + tl[db]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + r0 * C::RP + th[db]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+
   // query tiles: every head of the group, from the first tile with a row
   // that sees key k0
   const int kv_off = p.Nkv - p.Nq;
@@ -186,67 +187,80 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int T = p.group * nq;
   const float c = p.scale * kLog2e;
 
-  // staging registers for one tile (Q and dO rows, lse2, delta)
-  u32x4 st[C::LD];
+  // tile t: Q and dO rows by direct-to-LDS loads, lse2 / delta through
+  // registers (loaded at the top of the iteration before, stored at its end)
+  uint32_t voff[C::DMA];
+  dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
+  auto q_row0 = [&](int t) { return (int64_t)b * p.Hq + hk * p.group + t / nq; };
+  auto issue = [&](int t, int slot) {
+    const int q0 = (qt0 + t % nq) * C::BQ;
+    const int64_t slab = q_row0(t) * (int64_t)p.Nq * D;
+    const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
+    const i32x4 rq = sgpr_rsrc((const __bf16*)p.q + slab, (uint32_t)(p.Nq * C::RP));
+    const i32x4 ro = sgpr_rsrc((const __bf16*)p.dout + slab, (uint32_t)(p.Nq * C::RP));
+    dma_blocks<C::DMA>(rsrc_at(rq, (uint32_t)(q0 * C::RP)), dst, voff, wave);
+    dma_blocks<C::DMA>(rsrc_at(ro, (uint32_t)(q0 * C::RP)), dst + C::TILE, voff, wave);
+  };
   float st_l = 0.0f;
-  auto stage = [&](int t) {
-    const int hq = hk * p.group + t / nq;
-    const int q0 = (qt0 + t % nq) * C::BQ;
-    const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)p.q + q_slab * D, (uint32_t)(p.Nq * C::RP));
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const __bf16*)p.dout + q_slab * D, (uint32_t)(p.Nq * C::RP));
-#pragma unroll
-    for (int i = 0; i < C::LD; ++i) {
-      const int u = tid + i * C::NT;
-      const int which = u / (C::BQ * C::CH);
-      const int rem = u % (C::BQ * C::CH);
-      const uint32_t off = (uint32_t)((q0 + rem / C::CH) * C::RP + (rem % C::CH) * 16);
-      st[i] = which == 0 ? buf_load16(rq, off) : buf_load16(ro, off);
-    }
+  auto load_ld = [&](int t) {
     if (tid < 2 * C::BQ) {
-      const int r = q0 + (tid % C::BQ);
+      const int r = (qt0 + t % nq) * C::BQ + (tid % C::BQ);
+      const int64_t row = q_row0(t) * (int64_t)p.Nq + r;
       const bool live = r < p.Nq;
-      st_l = tid < C::BQ ? (live ? p.lse2[q_slab + r] : INFINITY) : (live ? p.delta[q_slab + r] : 0.0f);
+      st_l = tid < C::BQ ? (live ? p.lse2[row] : INFINITY) : (live ? p.delta[row] : 0.0f);
     }
   };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LD; ++i) {
-      const int u = tid + i * C::NT;
-      const int which = u / (C::BQ * C::CH);
-      const int rem = u % (C::BQ * C::CH);
-      const int row = rem / C::CH, ch = rem % C::CH;
-      lds_store16(which == 0 ? ldsQ : ldsO, (uint32_t)(row * C::RP + ((ch ^ rt_swz<D>(row)) << 4)), st[i]);
-    }
-    if (tid < 2 * C::BQ) ldsL[tid] = st_l;  // ldsD follows ldsL
+  auto store_ld = [&](int slot) {
+    if (tid < 2 * C::BQ) reinterpret_cast<float*>(lds + slot * C::SLOT + 2 * C::TILE)[tid] = st_l;
   };
 
-  if (T > 0) stage(0);
+  if (T > 0) {
+    issue(0, 0);
+    load_ld(0);
+    store_ld(0);
+  }
   for (int t = 0; t < T; ++t) {
+    const int slot = t & 1;
     const int q0 = (qt0 + t % nq) * C::BQ;
-    __syncthreads();  // the previous tile's LDS reads are done
-    commit();
-    __syncthreads();
-    if (t + 1 < T) stage(t + 1);
+    wait_vmem_all();
+    __syncthreads();  // tile t resident; the other slot (tile t-1) is free
+    if (t + 1 < T) {
+      issue(t + 1, slot ^ 1);
+      load_ld(t + 1);
+    }
+    const char* const tQ = lds + slot * C::SLOT;
+    const char* const tO = tQ + C::TILE;
+    const float* const tL = reinterpret_cast<const float*>(tQ + 2 * C::TILE);
+    const float* const tD = tL + C::BQ;
 
+    // S = Q K^T and dP = dO V^T of both 32-row blocks first, so that the
+    // exponentials of block 0 can run under the products of block 1
+    f32x16 s[2], dp[2];
+    bool act[2];
 #pragma unroll
-    for (int qb = 0; qb < C::BQ / 32; ++qb) {
-      const int r0 = q0 + 32 * qb;  // first query row of the block
-      // wave-uniform skips: rows past Nq, or every row above this wave's keys
-      if (r0 >= p.Nq) continue;
-      if (p.causal && r0 + 31 + kv_off < k0w) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r0 = q0 + 32 * qb;
+      act[qb] = r0 < p.Nq && !(p.causal && r0 + 31 + kv_off < k0w);
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
+      if (act[qb]) {
 #pragma unroll
-      for (int cc = 0; cc < C::NC; ++cc) {
-        s = mfma_bf16(row_frag<D>(ldsQ, 32 * qb + l32, 2 * cc + h), kreg[cc], s);
-        dp = mfma_bf16(row_frag<D>(ldsO, 32 * qb + l32, 2 * cc + h), vreg[cc], dp);
+        for (int cc = 0; cc < C::NC; ++cc) {
+          s[qb] = mfma_bf16(lds_load16(tQ, rf[cc] + qb * 32 * C::RP), kreg[cc], s[qb]);
+          dp[qb] = mfma_bf16(lds_load16(tO, rf[cc] + qb * 32 * C::RP), vreg[cc], dp[qb]);
+        }
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (!act[qb]) continue;
+      const int r0 = q0 + 32 * qb;
       // lse2 and delta of this lane's 16 rows: 32 qb + 8 j + 4 h + 0..3
       float L[16], Dl[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldsL + 32 * qb + 8 * j + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ldsD + 32 * qb + 8 * j + 4 * h);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + 32 * qb + 8 * j + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(tD + 32 * qb + 8 * j + 4 * h);
         L[4 * j + 0] = l4.x; L[4 * j + 1] = l4.y; L[4 * j + 2] = l4.z; L[4 * j + 3] = l4.w;
         Dl[4 * j + 0] = d4.x; Dl[4 * j + 1] = d4.y; Dl[4 * j + 2] = d4.z; Dl[4 * j + 3] = d4.w;
       }
@@ -254,10 +268,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       float pv[16], dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = exp2_fast(__builtin_fmaf(s[r], c, -L[r]));
+        float e = exp2_fast(__builtin_fmaf(s[qb][r], c, -L[r]));
         if (mask && key > r0 + 8 * (r / 4) + 4 * h + (r % 4) + kv_off) e = 0.0f;
         pv[r] = e;
-        dsv[r] = e * (dp[r] - Dl[r]);
+        dsv[r] = e * (dp[qb][r] - Dl[r]);
       }
       u32x4 pf[2], df[2];
 #pragma unroll
@@ -271,11 +285,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          adv[db] = mfma_bf16(tr_frag<D>(ldsO, 32 * qb + 16 * kc, db, lane), pf[kc], adv[db]);
-          adk[db] = mfma_bf16(tr_frag<D>(ldsQ, 32 * qb + 16 * kc, db, lane), df[kc], adk[db]);
+          adv[db] = mfma_bf16(trf(tO, 32 * qb + 16 * kc, db), pf[kc], adv[db]);
+          adk[db] = mfma_bf16(trf(tQ, 32 * qb + 16 * kc, db), df[kc], adk[db]);
         }
       }
     }
+    if (t + 1 < T) store_ld(slot ^ 1);
   }
 
   // ---- epilogue: lane = key, registers = d ----------------------------------------
@@ -304,27 +319,28 @@ struct QCfg {
   static constexpr int BR = 32 * NW;             // query rows per work-group
   static constexpr int BC = 64;                  // keys per LDS tile
   static constexpr int RP = 2 * D;
-  static constexpr int CH = RP / 16;
   static constexpr int NC = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int TILE = BC * RP;
-  static constexpr int LD = 2 * TILE / 16 / NT;
-  static constexpr int LDS = 2 * TILE;
-  static_assert((2 * TILE / 16) % NT == 0, "tiles must split evenly over the threads");
+  static constexpr int DMA = TILE / 1024 / NW;
+  static constexpr int SLOT = 2 * TILE;          // K, V
+  static constexpr int LDS = 2 * SLOT;
+  static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   using C = QCfg<D>;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-  char* const ldsK = lds;
-  char* const ldsV = lds + C::TILE;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const int g16 = lane >> 4, r16 = lane & 15;
 
   const int n_qt = (p.Nq + C::BR - 1) / C::BR;
   const int wg = xcd_remap(blockIdx.x, n_qt * p.B * p.Hq);
@@ -362,72 +378,71 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const int klim = p.causal ? min(p.Nkv - 1, qrow + kv_off) : p.Nkv - 1;  // last visible key
   const float c = p.scale * kLog2e;
 
+  uint32_t rf[C::NC], tl[C::NDB], th[C::NDB];
+#pragma unroll
+  for (int cc = 0; cc < C::NC; ++cc) rf[cc] = (uint32_t)(l32 * C::RP + (((2 * cc + h) ^ rt_swz<D>(l32)) << 4));
+  {
+    const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int chunk = db * 4 + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+      tl[db] = (uint32_t)(rlo * C::RP + ((chunk ^ rt_swz<D>(rlo)) << 4) + ((r16 & 1) << 3));
+      th[db] = (uint32_t)(rhi * C::RP + ((chunk ^ rt_swz<D>(rhi)) << 4) + ((r16 & 1) << 3));
+    }
+  }
+
   const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
-  u32x4 st[C::LD];
-  auto stage = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < C::LD; ++i) {
-      const int u = tid + i * C::NT;
-      const int which = u / (C::BC * C::CH);
-      const int rem = u % (C::BC * C::CH);
-      const uint32_t off = (uint32_t)((kt * C::BC + rem / C::CH) * C::RP + (rem % C::CH) * 16);
-      st[i] = which == 0 ? buf_load16(rk, off) : buf_load16(rv, off);
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LD; ++i) {
-      const int u = tid + i * C::NT;
-      const int which = u / (C::BC * C::CH);
-      const int rem = u % (C::BC * C::CH);
-      const int row = rem / C::CH, ch = rem % C::CH;
-      lds_store16(which == 0 ? ldsK : ldsV, (uint32_t)(row * C::RP + ((ch ^ rt_swz<D>(row)) << 4)), st[i]);
-    }
+  const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  uint32_t voff[C::DMA];
+  dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
+  auto issue = [&](int kt, int slot) {
+    const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
+    dma_blocks<C::DMA>(rsrc_at(rk, (uint32_t)(kt * C::TILE)), dst, voff, wave);
+    dma_blocks<C::DMA>(rsrc_at(rv, (uint32_t)(kt * C::TILE)), dst + C::TILE, voff, wave);
   };
 
-  if (n_kt > 0) stage(0);
+  if (n_kt > 0) issue(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
+    const int slot = kt & 1;
+    wait_vmem_all();
     __syncthreads();
-    commit();
-    __syncthreads();
-    if (kt + 1 < n_kt) stage(kt + 1);
+    if (kt + 1 < n_kt) issue(kt + 1, slot ^ 1);
     const int key0 = kt * C::BC;
     // wave-uniform: this wave's rows see none of the tile
     if (p.causal && key0 > q0w + 31 + kv_off) continue;
+    const char* const tK = lds + slot * C::SLOT;
+    const char* const tV = tK + C::TILE;
+    const bool mask = key0 + C::BC > p.Nkv || (p.causal && key0 + C::BC - 1 > q0w + kv_off);
 
-    f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < C::NC; ++cc) {
-        s[kb] = mfma_bf16(row_frag<D>(ldsK, 32 * kb + l32, 2 * cc + h), qreg[cc], s[kb]);
-        dp[kb] = mfma_bf16(row_frag<D>(ldsV, 32 * kb + l32, 2 * cc + h), oreg[cc], dp[kb]);
+        s = mfma_bf16(lds_load16(tK, rf[cc] + kb * 32 * C::RP), qreg[cc], s);
+        dp = mfma_bf16(lds_load16(tV, rf[cc] + kb * 32 * C::RP), oreg[cc], dp);
       }
-    }
-    const bool mask = key0 + C::BC - 1 > klim || key0 + C::BC > p.Nkv;
-    u32x4 df[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = exp2_fast(__builtin_fmaf(s[kb][r], c, -lq));
+        float e = exp2_fast(__builtin_fmaf(s[r], c, -lq));
         if (mask && key0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
-        dsv[r] = e * (dp[kb][r] - dq_row);
+        dsv[r] = e * (dp[r] - dq_row);
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        df[2 * kb + kc] = u32x4{pack_bf16x2(dsv[8 * kc + 0], dsv[8 * kc + 1]), pack_bf16x2(dsv[8 * kc + 2], dsv[8 * kc + 3]),
-                                pack_bf16x2(dsv[8 * kc + 4], dsv[8 * kc + 5]), pack_bf16x2(dsv[8 * kc + 6], dsv[8 * kc + 7])};
-    }
+      for (int kc = 0; kc < 2; ++kc) {
+        const u32x4 df = u32x4{pack_bf16x2(dsv[8 * kc + 0], dsv[8 * kc + 1]), pack_bf16x2(dsv[8 * kc + 2], dsv[8 * kc + 3]),
+                               pack_bf16x2(dsv[8 * kc + 4], dsv[8 * kc + 5]), pack_bf16x2(dsv[8 * kc + 6], dsv[8 * kc + 7])};
+        const int r0 = 32 * kb + 16 * kc;
 #pragma unroll
-    for (int s16 = 0; s16 < 4; ++s16) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) acc[db] = mfma_bf16(tr_frag<D>(ldsK, 16 * s16, db, lane), df[s16], acc[db]);
+        for (int db = 0; db < C::NDB; ++db) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tK + r0 * C::RP + tl[db]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tK + r0 * C::RP + th[db]));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          acc[db] = mfma_bf16(u32x4{l2.x, l2.y, h2.x, h2.y}, df, acc[db]);
+        }
+      }
     }
   }
 
