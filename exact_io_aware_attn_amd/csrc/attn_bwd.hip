@@ -64,6 +64,15 @@ __device__ __forceinline__ int rt_swz(int row) {
   }
 }
 
+// Keep an MFMA accumulator in accumulation registers at this point (an
+// empty asm that may modify it there): with both dK^T/dV^T and the S/dP
+// accumulators live, the allocator otherwise parks values in AGPRs and
+// shuttles them back and forth every tile.
+__device__ __forceinline__ void hold_acc(f32x16& x) { asm volatile("" : "+a"(x)); }
+// The same for an operand fragment that stays live for the whole kernel
+// (the MFMA reads its A/B operands from accumulation registers as well).
+__device__ __forceinline__ void hold_frag(u32x4& x) { asm volatile("" : "+a"(x)); }
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -147,6 +156,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int c = 0; c < C::NC; ++c) {
     kreg[c] = buf_load16(rk, (uint32_t)(key * C::RP + (2 * c + h) * 16));
     vreg[c] = buf_load16(rv, (uint32_t)(key * C::RP + (2 * c + h) * 16));
+    hold_frag(kreg[c]);
+    hold_frag(vreg[c]);
   }
 
   f32x16 adv[C::NDB], adk[C::NDB];
@@ -233,30 +244,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const float* const tL = reinterpret_cast<const float*>(tQ + 2 * C::TILE);
     const float* const tD = tL + C::BQ;
 
-    // S = Q K^T and dP = dO V^T of both 32-row blocks first, so that the
-    // exponentials of block 0 can run under the products of block 1
-    f32x16 s[2], dp[2];
-    bool act[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int r0 = q0 + 32 * qb;
-      act[qb] = r0 < p.Nq && !(p.causal && r0 + 31 + kv_off < k0w);
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-      if (act[qb]) {
-#pragma unroll
-        for (int cc = 0; cc < C::NC; ++cc) {
-          s[qb] = mfma_bf16(lds_load16(tQ, rf[cc] + qb * 32 * C::RP), kreg[cc], s[qb]);
-          dp[qb] = mfma_bf16(lds_load16(tO, rf[cc] + qb * 32 * C::RP), vreg[cc], dp[qb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (!act[qb]) continue;
-      const int r0 = q0 + 32 * qb;
-      // lse2 and delta of this lane's 16 rows: 32 qb + 8 j + 4 h + 0..3
-      float L[16], Dl[16];
+    // A software pipeline over the tile's two 32-row blocks, in steps of
+    // two MFMAs, so that one wave keeps the matrix pipe fed by itself:
+    //   A: S(0), dP(0)                      B: S(1), dP(1) + softmax of block 0
+    //   C: dV^T, dK^T += ... (0) + softmax of block 1      D: dV^T, dK^T += ... (1)
+    // LDS fragments are read W steps (row reads) or W2 steps (transposing
+    // reads) ahead, fragment g of a phase pair's sequence in slot g % W; scheduling fences keep the steps in order (otherwise
+    // the compiler sinks every read to just before its MFMA and the wave
+    // waits out each read's latency).  Both blocks are computed even when
+    // one is entirely masked (only on a causal tile crossing the diagonal):
+    // branches around the products cost accumulator copies.
+    constexpr int W = 3, W2 = 2, NS = 2 * C::NDB;  // NS: steps of phase C or D
+    constexpr int EB = 16 / C::NC, EC = 16 / NS;   // softmax elements per step in B, C
+    f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
+    u32x4 fq[W], fo[W];
+    u32x4 tq[W2], to[W2];
+    u32x4 pf[2][2], df[2][2];
+    float L[16], Dl[16];  // lse2 and delta of the block whose softmax runs next
+    auto rowA = [&](const char* tile, int qb, int cc) { return lds_load16(tile, rf[cc] + qb * 32 * C::RP); };
+    // step j of phase C/D: (kc, db) = (j / NDB, j % NDB)
+    auto tr_load = [&](int qb, int j, int w) {
+      const int r0 = 32 * qb + 16 * (j / C::NDB);
+      to[w] = trf(tO, r0, j % C::NDB);
+      tq[w] = trf(tQ, r0, j % C::NDB);
+    };
+    auto load_ld_block = [&](int qb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + 32 * qb + 8 * j + 4 * h);
@@ -264,32 +276,97 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         L[4 * j + 0] = l4.x; L[4 * j + 1] = l4.y; L[4 * j + 2] = l4.z; L[4 * j + 3] = l4.w;
         Dl[4 * j + 0] = d4.x; Dl[4 * j + 1] = d4.y; Dl[4 * j + 2] = d4.z; Dl[4 * j + 3] = d4.w;
       }
+    };
+    // softmax and dS of elements r .. r+1 (a packed pair) of block qb
+    auto soft2 = [&](int qb, int r, const f32x16& sv, const f32x16& dv) {
+      const int r0 = q0 + 32 * qb;
       const bool mask = p.causal && r0 + kv_off < k0w + 31;
-      float pv[16], dsv[16];
+      float e[2], d[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = exp2_fast(__builtin_fmaf(s[qb][r], c, -L[r]));
-        if (mask && key > r0 + 8 * (r / 4) + 4 * h + (r % 4) + kv_off) e = 0.0f;
-        pv[r] = e;
-        dsv[r] = e * (dp[qb][r] - Dl[r]);
+      for (int i = 0; i < 2; ++i) {
+        const int rr = r + i;
+        e[i] = exp2_fast(__builtin_fmaf(sv[rr], c, -L[rr]));
+        if (mask && key > r0 + 8 * (rr / 4) + 4 * h + (rr % 4) + kv_off) e[i] = 0.0f;
+        d[i] = e[i] * (dv[rr] - Dl[rr]);
       }
-      u32x4 pf[2], df[2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        pf[kc] = u32x4{pack_bf16x2(pv[8 * kc + 0], pv[8 * kc + 1]), pack_bf16x2(pv[8 * kc + 2], pv[8 * kc + 3]),
-                       pack_bf16x2(pv[8 * kc + 4], pv[8 * kc + 5]), pack_bf16x2(pv[8 * kc + 6], pv[8 * kc + 7])};
-        df[kc] = u32x4{pack_bf16x2(dsv[8 * kc + 0], dsv[8 * kc + 1]), pack_bf16x2(dsv[8 * kc + 2], dsv[8 * kc + 3]),
-                       pack_bf16x2(dsv[8 * kc + 4], dsv[8 * kc + 5]), pack_bf16x2(dsv[8 * kc + 6], dsv[8 * kc + 7])};
+      const uint32_t pe = pack_bf16x2(e[0], e[1]), pd = pack_bf16x2(d[0], d[1]);
+      const int kc = r / 8, comp = (r % 8) / 2;
+      if (comp == 0) { pf[qb][kc].x = pe; df[qb][kc].x = pd; }
+      else if (comp == 1) { pf[qb][kc].y = pe; df[qb][kc].y = pd; }
+      else if (comp == 2) { pf[qb][kc].z = pe; df[qb][kc].z = pd; }
+      else { pf[qb][kc].w = pe; df[qb][kc].w = pd; }
+    };
+
+    load_ld_block(0);
+    static_for<0, W>([&](auto iI) {
+      constexpr int i = decltype(iI)::value;
+      fq[i] = rowA(tQ, 0, i);
+      fo[i] = rowA(tO, 0, i);
+    });
+    // phase A
+    static_for<0, C::NC>([&](auto cI) {
+      constexpr int cc = decltype(cI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      s0 = mfma_bf16(fq[cc % W], kreg[cc], s0);
+      dp0 = mfma_bf16(fo[cc % W], vreg[cc], dp0);
+      hold_acc(s0);
+      hold_acc(dp0);
+      constexpr int n = cc + W;
+      if constexpr (n < C::NC) {
+        fq[cc % W] = rowA(tQ, 0, n);
+        fo[cc % W] = rowA(tO, 0, n);
+      } else {
+        fq[cc % W] = rowA(tQ, 1, n - C::NC);
+        fo[cc % W] = rowA(tO, 1, n - C::NC);
       }
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          adv[db] = mfma_bf16(trf(tO, 32 * qb + 16 * kc, db), pf[kc], adv[db]);
-          adk[db] = mfma_bf16(trf(tQ, 32 * qb + 16 * kc, db), df[kc], adk[db]);
-        }
+    });
+    // phase B
+    static_for<0, C::NC>([&](auto cI) {
+      constexpr int cc = decltype(cI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      // fragment g = NC + cc of the two blocks' sequence sits in slot g % W
+      s1 = mfma_bf16(fq[(C::NC + cc) % W], kreg[cc], s1);
+      dp1 = mfma_bf16(fo[(C::NC + cc) % W], vreg[cc], dp1);
+      hold_acc(s1);
+      hold_acc(dp1);
+      constexpr int n = cc + W;
+      if constexpr (n < C::NC) {
+        fq[(C::NC + cc) % W] = rowA(tQ, 1, n);
+        fo[(C::NC + cc) % W] = rowA(tO, 1, n);
       }
-    }
+      if constexpr (cc >= C::NC - W2) tr_load(0, cc - (C::NC - W2), cc - (C::NC - W2));
+#pragma unroll
+      for (int e = 0; e < EB; e += 2) soft2(0, cc * EB + e, s0, dp0);
+      if constexpr (cc == C::NC - 1) load_ld_block(1);  // block 0's values are used up
+    });
+    // phase C
+    static_for<0, NS>([&](auto jI) {
+      constexpr int j = decltype(jI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int db = j % C::NDB, kc = j / C::NDB;
+      adv[db] = mfma_bf16(to[j % W2], pf[0][kc], adv[db]);
+      adk[db] = mfma_bf16(tq[j % W2], df[0][kc], adk[db]);
+      hold_acc(adv[db]);
+      hold_acc(adk[db]);
+      constexpr int n = j + W2;
+      if constexpr (n < NS) tr_load(0, n, j % W2);
+      else tr_load(1, n - NS, j % W2);
+#pragma unroll
+      for (int e = 0; e < EC; e += 2) soft2(1, j * EC + e, s1, dp1);
+    });
+    // phase D
+    static_for<0, NS>([&](auto jI) {
+      constexpr int j = decltype(jI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int db = j % C::NDB, kc = j / C::NDB;
+      adv[db] = mfma_bf16(to[(NS + j) % W2], pf[1][kc], adv[db]);
+      adk[db] = mfma_bf16(tq[(NS + j) % W2], df[1][kc], adk[db]);
+      hold_acc(adv[db]);
+      hold_acc(adk[db]);
+      constexpr int n = j + W2;
+      if constexpr (n < NS) tr_load(1, n, (NS + j) % W2);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < T) store_ld(slot ^ 1);
   }
 
