@@ -21,6 +21,8 @@ quant          -- the fp8 input pipeline: signed Hadamard rotation of Q and K,
                   quantisation with one descale per 64-row block.
 backward       -- gradients dQ, dK, dV: the chain rule through the forward
                   definition, P materialised per head.
+fp8p           -- attention with e4m3 probabilities, one power-of-two scale
+                  per 64-key block of each row, exact or Lean P codes.
 
 Every function cites the passage of the source pages it follows, by page title
 and section.  No function here is "parity unpinned": each one is pinned by a
@@ -33,6 +35,7 @@ from .e4m3 import e4m3fn_decode, E4M3FN_MAX
 from .keyrange import attention_range, attention_range_head, key_range_mask, merge
 from .quant import dequantize_blocks, e4m3fn_encode, hadamard, quantize_blocks, rotation
 from .backward import attention_backward, attention_backward_head, probabilities_head, row_delta
+from .fp8p import fp8p_attention, fp8p_attention_head
 
 __all__ = [
     "attention",
@@ -55,4 +58,6 @@ __all__ = [
     "attention_backward_head",
     "probabilities_head",
     "row_delta",
+    "fp8p_attention",
+    "fp8p_attention_head",
 ]
