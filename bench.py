@@ -193,6 +193,11 @@ def make_step(w, dev_inp, out, lse):
 
         return bracket(lambda: A.fwd_splitkv(q, k, v, ns, causal=w.causal, scale=w.scale, descales=desc,
                                              workspace=ws, out=out, lse=lse))
+    if w.dtype == "fp8" and w.extra.get("p"):
+        q, k, v, dq, dk, dv = dev_inp
+        lean = w.extra["p"] == "lean"
+        return bracket(lambda: A.fwd_fp8_p(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, lean=lean, out=out,
+                                           lse=lse))
     if w.dtype == "fp8":
         q, k, v, dq, dk, dv = dev_inp
         return bracket(lambda: A.fwd_fp8(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse))
@@ -241,7 +246,10 @@ def cpu_baseline(w, host_inp, n_heads, seconds):
     done = 0
     t0 = time.perf_counter()
     for b, hq in order:
-        if is_bwd(w):
+        if w.dtype == "fp8" and w.extra.get("p"):
+            oracle.fp8p_attention_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), w.scale, w.causal,
+                                       lean=w.extra["p"] == "lean")
+        elif is_bwd(w):
             g = host_inp[3][b, hq].to(torch.float64).numpy()
             oracle.attention_backward_head(get_q(b, hq), get_k(b, hq // G), get_v(b, hq // G), g, w.scale,
                                            w.causal)
@@ -335,6 +343,10 @@ def main():
             "workload": w.name,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
             "causal": w.causal, "scale": "1/sqrt(D)", "inputs": INPUTS.get(w.dtype, "i.i.d. N(0,1), seed 0"),
+            **({"probabilities": "e4m3, one power-of-two scale per 64-key block, " +
+                                 ("Lean P codes" if w.extra["p"] == "lean" else "exact codes") +
+                                 "; P V and the row sum on the fp8 matrix instruction"}
+               if w.extra.get("p") else {}),
             **({"timed": "attn_bwd: delta/lse2 prep + dK/dV + dQ launches (forward outputs computed once, "
                          "before the timed steps); roofline over the whole backward"} if is_bwd(w) else {}),
             **({"timed": "block quantisation of Q, K (rotated) and V + block-scaled e4m3 attention; "

@@ -16,10 +16,11 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_P_E4M3, ATTN_P_E4M3_LEAN = 1, 2
 
 # every symbol include/attn.h declares
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
-            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd",
+            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_fp8_p",
             "attn_status_string",
             "attn_last_error", "attn_version")
 
@@ -62,6 +63,8 @@ def lib():
     L.attn_quantize_fp8.restype = ci
     L.attn_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
     L.attn_fwd_fp8_blocks.restype = ci
+    L.attn_fwd_fp8_p.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, ci, vp]
+    L.attn_fwd_fp8_p.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_bwd.argtypes = [vp] * 9 + [i64] * 6 + [ci, cf, ci, vp, ctypes.c_size_t, vp]
@@ -346,3 +349,31 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, dq=None
                           float(scale), ATTN_BF16, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_ptr(stream)))
     return dq, dk, dv
+
+
+def fwd_fp8_p(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=False, scale=None, lean=False,
+              out=None, lse=None, return_lse=True, stream=None):
+    """e4m3 attention with e4m3 probabilities (both products on the fp8
+    matrix instruction); ``lean`` selects Lean P codes.  bf16 O, fp32 LSE."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    for t in (q, k, v):
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError("fwd_fp8_p takes torch.float8_e4m3fn tensors")
+    ptrs = []
+    for d in (descale_q, descale_k, descale_v):
+        if d is None:
+            ptrs.append(None)
+            continue
+        if d.dtype != torch.float32 or not d.is_cuda or d.numel() < 1:
+            raise ValueError("descales must be float32 device tensors with one element")
+        ptrs.append(d.data_ptr())
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd_fp8_p(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, int(causal),
+                                float(scale), *ptrs, ATTN_P_E4M3_LEAN if lean else ATTN_P_E4M3, _stream_ptr(stream)))
+    return out, lse

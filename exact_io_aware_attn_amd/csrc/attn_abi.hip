@@ -35,7 +35,7 @@ struct Ranges {
 int run_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
                 const float* dq, const float* dk, const float* dv, const Ranges* ranges, attn_stream_t stream,
-                bool blk_scaled = false) {
+                bool blk_scaled = false, int p_mode = 0) {
   g_last_error[0] = '\0';
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL device pointers");
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
@@ -75,7 +75,16 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   // generic tiled kernel and every other D > 256 case on the split-D kernels;
   // both scale before masking.
   attn::LaunchFn fn = nullptr;
-  if (blk_scaled) {
+  if (p_mode != 0) {
+    // e4m3 probabilities: the fp8 P V kernel only
+    if (p_mode != ATTN_P_E4M3 && p_mode != ATTN_P_E4M3_LEAN)
+      return fail(ATTN_ERR_INVALID_ARG, "unknown p_mode %d", p_mode);
+    if (dtype == ATTN_FP8_E4M3 && scale > 0.0f && !blk_scaled) fn = attn::p8_launcher((int)D, p_mode == ATTN_P_E4M3_LEAN);
+    if (!fn)
+      return fail(ATTN_ERR_UNSUPPORTED, "e4m3 probabilities need e4m3 inputs, D in {64, 128} and scale > 0 (D=%lld)",
+                  (long long)D);
+  }
+  if (!fn && blk_scaled) {
     // block descales: the e4m3 direct-to-LDS kernel only
     if (scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
     if (!fn)
@@ -146,6 +155,17 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  const float* descale_q, const float* descale_k, const float* descale_v, attn_stream_t stream) {
   return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_FP8_E4M3, descale_q, descale_k,
                      descale_v, nullptr, stream);
+}
+
+int attn_fwd_fp8_p(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                   int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale,
+                   const float* descale_q, const float* descale_k, const float* descale_v, int p_mode,
+                   attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  if (p_mode != ATTN_P_E4M3 && p_mode != ATTN_P_E4M3_LEAN)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown p_mode %d", p_mode);
+  return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_FP8_E4M3, descale_q, descale_k,
+                     descale_v, nullptr, stream, false, p_mode);
 }
 
 int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,

@@ -96,6 +96,11 @@ struct MergeParams {
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
+// e4m3 Q/K/V with e4m3 probabilities: P V and the row sum on the fp8 matrix
+// instruction, one power-of-two P scale per 64-key tile of each row; exact
+// codes or Lean P codes.  D = 64 or 128, scale > 0, per-tensor descales.
+LaunchFn p8_launcher(int D, bool lean);
+
 // e4m3 block quantisation of S = B * H slabs of N x D bf16 rows (D = 64,
 // 128 or 256): codes (S, N, D), descales (S, ceil(N/64)); rows rotated by
 // diag(signs) H_D / sqrt(D) first when signs (D values of +-1) is not null.

@@ -111,6 +111,12 @@ WORKLOADS = {
     # key-range splitting is for; the same problem run plainly and split into
     # 8 key ranges (extra["n_splits"]; 512 work-groups, two per CU, the best
     # of 1..64 measured) merged by LSE.
+    # the same problem with e4m3 probabilities (both products on the fp8
+    # matrix instruction), exact or Lean P codes (extra["p"])
+    "fp8_p8_outlier": Workload("fp8_p8_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01,
+                               extra={"p": "e4m3"}),
+    "fp8_lean_outlier": Workload("fp8_lean_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01,
+                                 extra={"p": "lean"}),
     # the fp8 input pipeline on the same problem: bf16 Q, K, V with the same
     # outlier channels, quantised on the device with one descale per 64-row
     # block, Q and K rotated by a signed Hadamard matrix first
@@ -163,6 +169,15 @@ def make_inputs(w: Workload):
         code, d = quantize_e4m3(x)
         out.append(code)
         desc.append(d)
+    if w.extra.get("qk_codes") == "narrow":
+        # Q and K codes of magnitude in [1/2, 4) with random signs (descale
+        # 1/4 each): every product is a multiple of 2^-8 below 16, so q . k
+        # is exact in float32 whatever the summation order
+        for i, x in enumerate((q, k)):
+            mag = rng.integers(6 * 8, 9 * 8, size=x.shape)          # exponent field 6..8, any mantissa
+            sign = rng.integers(0, 2, size=x.shape) << 7
+            out[i] = torch.from_numpy((mag | sign).astype(np.uint8)).view(torch.float8_e4m3fn)
+            desc[i] = np.float32(0.25)
     return out[0], out[1], out[2], np.array(desc, dtype=np.float32)
 
 

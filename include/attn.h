@@ -131,6 +131,33 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
  *     LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p.
  */
 
+/* Probability precision of attn_fwd_fp8_p (the P of P V). */
+typedef enum {
+  ATTN_P_E4M3 = 1,      /* e4m3 codes of 2^(x - E), nearest, ties to even */
+  ATTN_P_E4M3_LEAN = 2  /* Lean P codes rne(8 (x - E) + 56): no exponential */
+} attn_p_mode;
+
+/*
+ * attn_fwd_fp8_p -- attn_fwd_fp8 with e4m3 probabilities, so that both
+ * products run on the fp8 matrix instruction (ZYFA article, section "The
+ * three techniques, in plain terms": per-block scaling with a rounded row
+ * sum, and Lean P).  Not exact attention: each probability is rounded to
+ * e4m3.  With base-2 scores x_ij = scale dq dk log2(e) (q8_i . k8_j), for
+ * each row and each 64-key block b (keys [64 b, 64 b + 64)):
+ *   E = ceil(max over the block's visible keys of x_ij) - 8,
+ *   p_ij = decode(code_ij) 2^E with code_ij as `p_mode` says,
+ *   O_i = dv sum_j p_ij v8_j / sum_j p_ij,  LSE_i = ln sum_j p_ij
+ * (the row sum is taken from the same rounded p_ij, on the matrix unit).
+ *   p_mode : ATTN_P_E4M3 or ATTN_P_E4M3_LEAN
+ * D = 64 or 128, scale > 0; other arguments, outputs and errors as
+ * attn_fwd_fp8.
+ */
+int attn_fwd_fp8_p(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                   int causal, float scale,
+                   const float* descale_q, const float* descale_k, const float* descale_v,
+                   int p_mode, attn_stream_t stream);
+
 /*
  * attn_fwd_partial -- attention over the keys kv_begin <= j < kv_end only.
  *   q, k, v, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype: as attn_fwd; k and

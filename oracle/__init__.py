@@ -35,7 +35,7 @@ from .e4m3 import e4m3fn_decode, E4M3FN_MAX
 from .keyrange import attention_range, attention_range_head, key_range_mask, merge
 from .quant import dequantize_blocks, e4m3fn_encode, hadamard, quantize_blocks, rotation
 from .backward import attention_backward, attention_backward_head, probabilities_head, row_delta
-from .fp8p import fp8p_attention, fp8p_attention_head
+from .fp8p import fp8p_attention, fp8p_attention_head, fp8p_attention_head_f32
 
 __all__ = [
     "attention",
@@ -60,4 +60,5 @@ __all__ = [
     "row_delta",
     "fp8p_attention",
     "fp8p_attention_head",
+    "fp8p_attention_head_f32",
 ]

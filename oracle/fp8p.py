@@ -31,6 +31,11 @@ What is computed, for one row i (readings where the article is silent):
   O_i   = sum_j p_ij v_j / sum_j p_ij,   LSE_i = ln(sum_j p_ij)
 A row that sees no key has O = 0, LSE = -inf.  p_ij approximates
 exp(scale q_i . k_j) itself, so no running maximum appears in the result.
+
+``fp8p_attention_head_f32`` takes the same rounding decisions (block
+exponent, code) from float32 values computed as the device computes them
+(one rounding after each multiply-add), for parity at the level of
+individual codes; its inputs must keep q . k exact in float32.
 """
 import numpy as np
 
@@ -112,4 +117,56 @@ def fp8p_attention(q, k, v, scale, causal=False, lean=False):
         for hq in range(Hq):
             hk = kv_head_of(hq, Hq, Hkv)
             O[b, hq], lse[b, hq] = fp8p_attention_head(q[b, hq], k[b, hk], v[b, hk], scale, causal, lean)
+    return O, lse
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def fp8p_attention_head_f32(q, k, v, c32, causal=False, lean=False, rows=None, block=BLOCK):
+    """The weights of ``fp8p_attention_head`` with every rounding decision
+    taken in float32, as the device takes it:
+      s_ij  = q_i . k_j (q, k the e4m3 values without descales; the caller
+              keeps these sums exact in float32),
+      c32   = the float32 multiplier scale * log2(e) * dq * dk,
+      E     = ceil(f32(max_j s_ij * c32)) - 8 per 64-key block,
+      exact: code = e4m3(2^f32(s_ij c32 - E))  (one rounding: a multiply-add)
+      lean:  code = rne(f32(s_ij f32(8 c32) + f32(56 - 8 E))), clamped to [0, 126]
+    and O, LSE as ``fp8p_attention_head`` (v carries its descale)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    c32 = float(np.float32(c32))
+    Nq, Nkv = q.shape[0], k.shape[0]
+    if rows is None:
+        rows = np.arange(Nq)
+    rows = np.asarray(rows, dtype=np.int64)
+    vis = visible_mask(Nq, Nkv, causal, rows)
+    S = q[rows] @ k.T                                   # exact by the caller's choice of inputs
+    R, N = S.shape
+    nb = (N + block - 1) // block
+    w = np.zeros((R, N))
+    Ej = np.zeros((R, N))
+    for b in range(nb):
+        sl = slice(b * block, min((b + 1) * block, N))
+        vb = vis[:, sl]
+        smax = np.where(vb, S[:, sl], -np.inf).max(axis=1)
+        has = np.isfinite(smax)
+        E = np.where(has, np.ceil(_f32(np.where(has, smax, 0.0) * c32)) - TOP, 0.0)
+        if lean:
+            c8 = float(np.float32(8.0 * c32))
+            y = _f32(S[:, sl] * c8 + _f32(LEAN_BIAS - 8.0 * E)[:, None])
+            codes = np.clip(np.rint(y), 0, 126).astype(np.uint8)
+        else:
+            y = _f32(S[:, sl] * c32 - E[:, None])
+            codes = e4m3fn_encode(np.exp2(y))
+        w[:, sl] = np.where(vb, e4m3fn_decode(codes), 0.0)
+        Ej[:, sl] = E[:, None]
+    any_vis = vis.any(axis=1)
+    Emax = np.where(any_vis, np.where(vis, Ej, -np.inf).max(axis=1), 0.0)
+    p = w * np.exp2(np.where(vis, Ej - Emax[:, None], 0.0))
+    l = p.sum(axis=1)
+    O = np.where(any_vis[:, None] & (l[:, None] > 0), (p @ v) / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    lse = np.where(any_vis & (l > 0), (np.log2(np.where(l > 0, l, 1.0)) + Emax) / LOG2E, -np.inf)
     return O, lse

@@ -123,7 +123,45 @@ def check_error_statistics():
     return ok
 
 
-ALL_CHECKS = [check_integer_scores_are_exact, check_hand_worked_row, check_block_exponents, check_error_statistics]
+def check_f32_decisions():
+    """The float32-decision form agrees with the float64 form where float32
+    rounding is exact (integer scores, c = 1), and with a float32 hand
+    computation of one row otherwise."""
+    ok = True
+    rng = np.random.default_rng(2)
+    x = rng.integers(-5, 9, size=150).astype(np.float64)
+    v = rng.standard_normal((150, 3))
+    q, k, vv, _ = one_row(x, v)
+    for lean in (False, True):
+        O64, L64 = ofp.fp8p_attention_head(q, k, vv, 1.0 / LOG2E, lean=lean)
+        O32, L32 = ofp.fp8p_attention_head_f32(q, k, vv, 1.0, lean=lean)
+        ok &= np.allclose(O64, O32, rtol=0, atol=1e-12) and abs(L64[0] - L32[0]) <= 1e-12
+    # one row by hand in float32: scores s, multiplier c
+    s = rng.integers(-300, 300, size=70).astype(np.float64) / 16.0
+    c = np.float32(0.0912)
+    q, k, vv, _ = one_row(s, rng.standard_normal((70, 2)))
+    for lean in (False, True):
+        num, den = np.zeros(2), 0.0
+        for b0 in range(0, 70, 64):
+            sb = s[b0:b0 + 64]
+            E = math.ceil(float(np.float32(np.float32(sb.max()) * c))) - 8
+            for j, sj in enumerate(sb):
+                if lean:
+                    y = np.float32(np.float64(sj) * np.float64(np.float32(8 * c)) + (56.0 - 8 * E))
+                    cde = int(min(max(np.rint(y), 0), 126))
+                    wgt = decode_e4m3(cde)
+                else:
+                    y = np.float32(np.float64(sj) * np.float64(c) - E)
+                    wgt = float(torch.tensor([2.0 ** float(y)], dtype=torch.float64).to(torch.float8_e4m3fn).double()[0])
+                num += wgt * 2.0 ** E * vv[b0 + j]
+                den += wgt * 2.0 ** E
+        O, L = ofp.fp8p_attention_head_f32(q, k, vv, c, lean=lean)
+        ok &= np.allclose(O[0], num / den, rtol=1e-12, atol=1e-12) and abs(L[0] - math.log(den)) <= 1e-12
+    return ok
+
+
+ALL_CHECKS = [check_integer_scores_are_exact, check_hand_worked_row, check_block_exponents, check_error_statistics,
+              check_f32_decisions]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
