@@ -202,6 +202,8 @@ def make_step(w, dev_inp, out, lse):
         q, k, v, dq, dk, dv = dev_inp
         return bracket(lambda: A.fwd_fp8(q, k, v, dq, dk, dv, causal=w.causal, scale=w.scale, out=out, lse=lse))
     q, k, v = dev_inp
+    if w.extra.get("exp") == "poly":
+        return bracket(lambda: A.fwd_exp_poly(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse))
     return bracket(lambda: A.fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse))
 
 
@@ -343,6 +345,8 @@ def main():
             "workload": w.name,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
             "causal": w.causal, "scale": "1/sqrt(D)", "inputs": INPUTS.get(w.dtype, "i.i.d. N(0,1), seed 0"),
+            **({"exponential": "cubic polynomial on the FMA pipe (relative error <= 8.6e-5)"}
+               if w.extra.get("exp") == "poly" else {}),
             **({"probabilities": "e4m3, one power-of-two scale per 64-key block, " +
                                  ("Lean P codes" if w.extra["p"] == "lean" else "exact codes") +
                                  "; P V and the row sum on the fp8 matrix instruction"}

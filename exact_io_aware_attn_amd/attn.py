@@ -20,7 +20,7 @@ ATTN_P_E4M3, ATTN_P_E4M3_LEAN = 1, 2
 
 # every symbol include/attn.h declares
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
-            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_fp8_p",
+            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_fp8_p", "attn_fwd_exp_poly",
             "attn_status_string",
             "attn_last_error", "attn_version")
 
@@ -63,6 +63,8 @@ def lib():
     L.attn_quantize_fp8.restype = ci
     L.attn_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
     L.attn_fwd_fp8_blocks.restype = ci
+    L.attn_fwd_exp_poly.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp]
+    L.attn_fwd_exp_poly.restype = ci
     L.attn_fwd_fp8_p.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, ci, vp]
     L.attn_fwd_fp8_p.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
@@ -376,4 +378,23 @@ def fwd_fp8_p(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=Fa
     _check(lib().attn_fwd_fp8_p(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, int(causal),
                                 float(scale), *ptrs, ATTN_P_E4M3_LEAN if lean else ATTN_P_E4M3, _stream_ptr(stream)))
+    return out, lse
+
+
+def fwd_exp_poly(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True, stream=None):
+    """bf16 attention with the probabilities' exponentials from a cubic
+    polynomial (relative error <= 8.6e-5) instead of the transcendental unit."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("fwd_exp_poly takes bfloat16 tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd_exp_poly(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, int(causal),
+                                   float(scale), _stream_ptr(stream)))
     return out, lse

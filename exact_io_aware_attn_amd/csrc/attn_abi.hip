@@ -35,7 +35,7 @@ struct Ranges {
 int run_forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
                 const float* dq, const float* dk, const float* dv, const Ranges* ranges, attn_stream_t stream,
-                bool blk_scaled = false, int p_mode = 0) {
+                bool blk_scaled = false, int p_mode = 0, bool poly = false) {
   g_last_error[0] = '\0';
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL device pointers");
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
@@ -82,6 +82,12 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
     if (dtype == ATTN_FP8_E4M3 && scale > 0.0f && !blk_scaled) fn = attn::p8_launcher((int)D, p_mode == ATTN_P_E4M3_LEAN);
     if (!fn)
       return fail(ATTN_ERR_UNSUPPORTED, "e4m3 probabilities need e4m3 inputs, D in {64, 128} and scale > 0 (D=%lld)",
+                  (long long)D);
+  }
+  if (poly) {
+    if (dtype == ATTN_BF16 && scale > 0.0f) fn = attn::pipe_poly_launcher((int)D);
+    if (!fn)
+      return fail(ATTN_ERR_UNSUPPORTED, "the polynomial exponential needs bf16, D in {64, 128} and scale > 0 (D=%lld)",
                   (long long)D);
   }
   if (!fn && blk_scaled) {
@@ -166,6 +172,14 @@ int attn_fwd_fp8_p(const void* q, const void* k, const void* v, void* o, float* 
     return fail(ATTN_ERR_INVALID_ARG, "unknown p_mode %d", p_mode);
   return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_FP8_E4M3, descale_q, descale_k,
                      descale_v, nullptr, stream, false, p_mode);
+}
+
+int attn_fwd_exp_poly(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale,
+                      attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  return run_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, ATTN_BF16, nullptr, nullptr, nullptr,
+                     nullptr, stream, false, 0, true);
 }
 
 int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,

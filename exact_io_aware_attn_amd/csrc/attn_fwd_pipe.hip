@@ -97,7 +97,21 @@ struct PipeCfg {
   static_assert(!LARGE || FP8, "bf16 beyond D = 128 runs the wide-head kernel");
 };
 
-template <int E, int D, int NW, int NBUF, int BC>
+// 2^y by a polynomial on the FMA pipe instead of v_exp_f32 (blog post
+// "FlashAttention v1/v2/v3/v4", table of ideas: FA4 computes part of the
+// exponentials with a polynomial): y = j + f with j = floor(y), 2^f from a
+// cubic fitted to minimise the relative error on [0, 1) (at most 8.6e-5,
+// below bf16's 2^-9), then scaled by 2^j (v_ldexp; y below -200, -inf
+// included, gives 0).
+__device__ __forceinline__ float poly_exp2(float y) {
+  y = fmaxf(y, -200.0f);
+  const float j = __builtin_floorf(y);
+  const float f = y - j;
+  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(0.07706515f, f, 0.22764705f), f, 0.69511634f), f, 1.0f);
+  return __builtin_ldexpf(p, (int)j);
+}
+
+template <int E, int D, int NW, int NBUF, int BC, bool POLY = false>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_fwd_pipe_kernel(FwdParams p) {
   using C = PipeCfg<E, D, NW, NBUF, BC>;
   constexpr bool FP8 = C::FP8;
@@ -462,7 +476,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
         const int kb = s16 >> 1, r0 = (s16 & 1) * 8;
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(s[qb][kb][r0 + i], ct, mneg));
+        for (int i = 0; i < 8; ++i) {
+          const float y = __builtin_fmaf(s[qb][kb][r0 + i], ct, mneg);
+          e[i] = POLY ? poly_exp2(y) : exp2_fast(y);
+        }
         pf[qb][s16].x = pack_bf16x2(e[0], e[1]);
         pf[qb][s16].y = pack_bf16x2(e[2], e[3]);
         pf[qb][s16].z = pack_bf16x2(e[4], e[5]);
@@ -544,7 +561,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   }
 }
 
-template <int E, int D, int NW, int NBUF, int BC>
+template <int E, int D, int NW, int NBUF, int BC, bool POLY = false>
 hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   using C = PipeCfg<E, D, NW, NBUF, BC>;
   FwdParams p = p0;
@@ -552,7 +569,7 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_pipe_kernel<E, D, NW, NBUF, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<E, D, NW, NBUF, BC, POLY>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -573,6 +590,14 @@ LaunchFn pipe_launcher(int elt, int D) {
     // two work-groups of 4 waves per CU, 64-key tiles, double-buffered
     case 64: return &launch_pipe<ELT_BF16, 64, 4, 2, 64>;
     case 128: return &launch_pipe<ELT_BF16, 128, 4, 2, 64>;
+    default: return nullptr;
+  }
+}
+
+LaunchFn pipe_poly_launcher(int D) {
+  switch (D) {
+    case 64: return &launch_pipe<ELT_BF16, 64, 4, 2, 64, true>;
+    case 128: return &launch_pipe<ELT_BF16, 128, 4, 2, 64, true>;
     default: return nullptr;
   }
 }

@@ -101,6 +101,10 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 // codes or Lean P codes.  D = 64 or 128, scale > 0, per-tensor descales.
 LaunchFn p8_launcher(int D, bool lean);
 
+// bf16 direct-to-LDS kernel with the probabilities' exponentials from a cubic
+// polynomial on the FMA pipe (D = 64 or 128, scale > 0).
+LaunchFn pipe_poly_launcher(int D);
+
 // e4m3 block quantisation of S = B * H slabs of N x D bf16 rows (D = 64,
 // 128 or 256): codes (S, N, D), descales (S, ceil(N/64)); rows rotated by
 // diag(signs) H_D / sqrt(D) first when signs (D values of +-1) is not null.

@@ -101,6 +101,10 @@ WORKLOADS = {
     },
     # fp8 e4m3 diffusion-style attention with 1% outlier channels
     "fp8_outlier": Workload("fp8_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01),
+    # the causal prefill with the probabilities' exponentials from a cubic
+    # polynomial instead of the transcendental unit (extra["exp"])
+    "prefill_causal_bf16_poly": Workload("prefill_causal_bf16_poly", 4, 32, 32, 4096, 4096, 128, True, "bf16",
+                                         extra={"exp": "poly"}),
     # the backward pass of the causal prefill problem (extra["pass"]): dQ, dK,
     # dV from Q, K, V, the forward O and LSE and an upstream dO
     "bwd_causal_bf16": Workload("bwd_causal_bf16", 4, 32, 32, 4096, 4096, 128, True, "bf16",

@@ -159,6 +159,20 @@ int attn_fwd_fp8_p(const void* q, const void* k, const void* v, void* o, float* 
                    int p_mode, attn_stream_t stream);
 
 /*
+ * attn_fwd_exp_poly -- attn_fwd (bf16) with each probability's exponential
+ * computed by a polynomial on the FMA pipe instead of the transcendental
+ * instruction (blog post "FlashAttention v1/v2/v3/v4", table of ideas: FA4's
+ * polynomial exponential): 2^y = 2^floor(y) p(y - floor(y)) with the cubic
+ * p(f) = 1 + 0.69511634 f + 0.22764705 f^2 + 0.07706515 f^3, relative error
+ * at most 8.6e-5 on [0, 1).  Inexact only by that error, below bf16
+ * rounding.  bf16 q, k, v, o; D = 64 or 128; scale > 0; outputs and errors as
+ * attn_fwd.
+ */
+int attn_fwd_exp_poly(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                      int causal, float scale, attn_stream_t stream);
+
+/*
  * attn_fwd_partial -- attention over the keys kv_begin <= j < kv_end only.
  *   q, k, v, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype: as attn_fwd; k and
  *            v hold the whole Nkv-key sequence and the causal mask keeps the

@@ -23,6 +23,7 @@ backward       -- gradients dQ, dK, dV: the chain rule through the forward
                   definition, P materialised per head.
 fp8p           -- attention with e4m3 probabilities, one power-of-two scale
                   per 64-key block of each row, exact or Lean P codes.
+polyexp        -- the cubic base-2 exponential of the polynomial-exp variant.
 
 Every function cites the passage of the source pages it follows, by page title
 and section.  No function here is "parity unpinned": each one is pinned by a
@@ -36,6 +37,7 @@ from .keyrange import attention_range, attention_range_head, key_range_mask, mer
 from .quant import dequantize_blocks, e4m3fn_encode, hadamard, quantize_blocks, rotation
 from .backward import attention_backward, attention_backward_head, probabilities_head, row_delta
 from .fp8p import fp8p_attention, fp8p_attention_head, fp8p_attention_head_f32
+from .polyexp import poly_exp2
 
 __all__ = [
     "attention",
@@ -61,4 +63,5 @@ __all__ = [
     "fp8p_attention",
     "fp8p_attention_head",
     "fp8p_attention_head_f32",
+    "poly_exp2",
 ]

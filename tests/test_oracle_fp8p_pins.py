@@ -216,3 +216,23 @@ def test_fp8p_planted_mistakes_are_caught(name, monkeypatch):
     monkeypatch.setattr(mod, attr, fn)
     failed = [c.__name__ for c in ALL_CHECKS if not c()]
     assert failed, f"no check caught the planted mistake {name}"
+
+
+def test_poly_exp2_error_bound():
+    """The cubic meets its stated bound against numpy's exp2 (relative error
+    at most 8.6e-5 over a dense grid of [-126, 8]), is exact at integers
+    (f = 0), and underflows to 0 at -150 and below, -inf included."""
+    y = np.linspace(-126.0, 8.0, 2_000_001)
+    rel = np.abs(oracle.poly_exp2(y) / np.exp2(y) - 1.0)
+    assert rel.max() <= 8.6e-5
+    ints = np.arange(-126, 9, dtype=np.float64)
+    assert np.array_equal(oracle.poly_exp2(ints), np.exp2(ints))
+    assert oracle.poly_exp2(np.array([-250.0, -np.inf])).tolist() == [0.0, 0.0]
+
+
+def test_poly_exp2_planted_mistake_is_caught(monkeypatch):
+    """A coefficient slip (b and c swapped) breaks the bound."""
+    import oracle.polyexp as ope
+    monkeypatch.setattr(ope, "COEFFS", (ope.COEFFS[0], ope.COEFFS[2], ope.COEFFS[1]))
+    y = np.linspace(-10.0, 8.0, 100_001)
+    assert np.abs(ope.poly_exp2(y) / np.exp2(y) - 1.0).max() > 8.6e-5
