@@ -59,22 +59,29 @@ INPUTS = {
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_io_aware_attn_amd", "csrc")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "85bbcbeb41fc2cb8",
-                            200695.5625 * 2 * 1024, 133140.5 * 1024),
-    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "85bbcbeb41fc2cb8",
-                    188131.25 * 2 * 1024, 99840.0 * 1024),
+    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
+                            200581.4375 * 2 * 1024, 133139.0625 * 1024),
+    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
+                    188231.9375 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once: 49201 KiB fetched, 49344 KiB written per call)
-    "fp8_blocks_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "85bbcbeb41fc2cb8",
-                           189102.90625 * 2 * 1024, 99840.0 * 1024),
+    "fp8_blocks_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
+                           189063.1875 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "b1a4527d429ab446",
                           164165.5 * 2 * 1024, 65664.0 * 1024),
     "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
-    # it reads 16929 KiB x 2 and writes 2080 KiB)
-    "chunk_prefill_splitkv_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "85bbcbeb41fc2cb8",
+    # it reads 16928 KiB x 2 and writes 2080 KiB)
+    "chunk_prefill_splitkv_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
                                    73790.0 * 2 * 1024, 33024.0 * 1024),
+    # the whole backward step: prep + dK/dV + dQ launches
+    "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_bwd.hip"), "be68a3764dc561f0",
+                        (133131.0 + 264286.0 + 266836.90625) * 2 * 1024, (4096.0 + 262144.125 + 131082.421875) * 1024),
+    "fp8_p8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_p8.hip"), "659f97eb1470c201",
+                       189136.9375 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_p8.hip"), "659f97eb1470c201",
+                         172636.40625 * 2 * 1024, 99840.0 * 1024),
 }
 
 
