@@ -121,6 +121,13 @@ WORKLOADS = {
                                extra={"p": "e4m3"}),
     "fp8_lean_outlier": Workload("fp8_lean_outlier", 1, 24, 24, 16384, 16384, 128, False, "fp8", outlier_frac=0.01,
                                  extra={"p": "lean"}),
+    # the configuration the ZYFA article quotes its fp8 figure on: causal
+    # prefill, 32K tokens, D = 128, Gaussian inputs (the article gives no head
+    # count; 32 heads of 128, a 4096-wide model); e4m3 P, exact or Lean codes
+    "fp8_p8_causal_32k": Workload("fp8_p8_causal_32k", 1, 32, 32, 32768, 32768, 128, True, "fp8",
+                                  extra={"p": "e4m3"}),
+    "fp8_lean_causal_32k": Workload("fp8_lean_causal_32k", 1, 32, 32, 32768, 32768, 128, True, "fp8",
+                                    extra={"p": "lean"}),
     # the fp8 input pipeline on the same problem: bf16 Q, K, V with the same
     # outlier channels, quantised on the device with one descale per 64-row
     # block, Q and K rotated by a signed Hadamard matrix first
