@@ -137,12 +137,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 
   // work decomposition: the key tiles of one (batch, KV head) are
   // neighbours, so they run together on one XCD and share its Q/dO in L2
+  // (causal, paired: key tiles i and n-1-i, the heavier first)
   const int n_kt = (p.Nkv + C::BK - 1) / C::BK;
-  const int wg = xcd_remap(blockIdx.x, n_kt * p.B * p.Hkv);
-  const int kt = wg % n_kt;
-  const int bh = wg / n_kt;
+  const int nslot = p.pair_kv ? (n_kt + 1) / 2 : n_kt;
+  const int wg = xcd_remap(blockIdx.x, nslot * p.B * p.Hkv);
+  const int slot_k = wg % nslot;
+  const int bh = wg / nslot;
   const int hk = bh % p.Hkv;
   const int b = bh / p.Hkv;
+  const int njobs = (p.pair_kv && 2 * slot_k + 1 != n_kt) ? 2 : 1;
+  for (int job = 0; job < njobs; ++job) {
+  if (job > 0) __syncthreads();  // every wave is done with the LDS of the first tile
+  const int kt = job == 0 ? slot_k : n_kt - 1 - slot_k;
   const int k0 = kt * C::BK;
   const int k0w = k0 + 32 * wave;
   const int key = k0w + l32;
@@ -385,6 +391,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     }
   }
+}  // job
 }
 
 // ---- dQ -------------------------------------------------------------------------------
@@ -538,11 +545,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D>
-hipError_t launch(const BwdParams& p, hipStream_t stream) {
+hipError_t launch(const BwdParams& p0, hipStream_t stream) {
+  BwdParams p = p0;
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   const int64_t prep_wg = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
-  const int64_t kv_wg = (int64_t)((p.Nkv + KVCfg<D>::BK - 1) / KVCfg<D>::BK) * p.B * p.Hkv;
-  const int64_t q_wg = (int64_t)((p.Nq + QCfg<D>::BR - 1) / QCfg<D>::BR) * p.B * p.Hq;
+  const int n_kt = (p.Nkv + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
+  const int n_qt = (p.Nq + QCfg<D>::BR - 1) / QCfg<D>::BR;
+  p.pair_kv = pair_causal_grid(p.causal, (int64_t)p.B * p.Hkv, n_kt, p.Nq, p.Nkv);
+  const int64_t kv_wg = (int64_t)(p.pair_kv ? (n_kt + 1) / 2 : n_kt) * p.B * p.Hkv;
+  const int64_t q_wg = (int64_t)n_qt * p.B * p.Hq;
   if (prep_wg >= ((int64_t)1 << 31) || kv_wg >= ((int64_t)1 << 31) || q_wg >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)prep_wg), dim3(256), 0, stream, p);

@@ -135,11 +135,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
   const int split = wg_all / per_split;  // key range (split-KV); 0 for a plain call
   const int wg = wg_all - split * per_split;
   const KeyRange kr = key_range(p, split);
-  const int qt_raw = wg % p.n_qtiles;
-  const int bh = wg / p.n_qtiles;
+  // one query tile per work-group, or a causal pair n-1-i, i (largest first)
+  const int nslot = qtile_slots(p);
+  const int slot_q = wg % nslot;
+  const int bh = wg / nslot;
   const int hq = bh % p.Hq;
   const int b = bh / p.Hq;
-  const int qt = p.causal ? (p.n_qtiles - 1 - qt_raw) : qt_raw;
+  const int njobs = (p.pair_causal && 2 * slot_q + 1 != p.n_qtiles) ? 2 : 1;
+  for (int job = 0; job < njobs; ++job) {
+  if (job > 0) __syncthreads();  // every wave is done with the LDS of the first tile
+  const int qt = (p.causal && job == 0) ? (p.n_qtiles - 1 - slot_q) : slot_q;
   const int hk = hq / p.group;
   const int q0 = qt * C::BR;
   const int q0w = q0 + wave * C::QW;
@@ -559,6 +564,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
             l_tot > 0.0f ? (m_run[qb] + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
+}  // job
 }
 
 template <int E, int D, int NW, int NBUF, int BC, bool POLY = false>
@@ -566,7 +572,8 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   using C = PipeCfg<E, D, NW, NBUF, BC>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
+  p.pair_causal = pair_causal_tiles(p);
+  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<E, D, NW, NBUF, BC, POLY>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 // Arguments of one forward call after validation.  Sizes are int: the ABI
@@ -21,7 +23,7 @@ struct FwdParams {
   int causal;          // 0 or 1
   int kv_off;          // Nkv - Nq: key j visible to query i iff j <= i + kv_off
   int n_qtiles;        // filled by the launcher
-  int total_wg;        // filled by the launcher: n_splits * B * Hq * n_qtiles
+  int total_wg;        // filled by the launcher: n_splits * B * Hq * (query tiles or pairs)
   float scale;         // multiplier of Q K^T
   const float* dq;     // fp8 descales (device pointers) or null
   const float* dk;
@@ -42,6 +44,9 @@ struct FwdParams {
   // e4m3 with one descale per 64-row block (a plain key range only): dq
   // points at (B, Hq, ceil(Nq/64)) floats, dk and dv at (B, Hkv, ceil(Nkv/64))
   int blk_scaled;
+  // causal query tiles paired first with last in one work-group (set by the
+  // direct-to-LDS kernel's launcher)
+  int pair_causal;
 };
 
 // The keys one work-group attends to: nkv keys starting at row k0 of its
@@ -60,6 +65,44 @@ __device__ __forceinline__ KeyRange key_range(const FwdParams& p, int split) {
 }
 
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
+
+// Compute units of the current device, queried once per device (256 on
+// MI355X; that value if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Causal tiles paired first with last (the ZYFA article, "The details that
+// make it production-grade"): work-group i of a head runs tiles i and n-1-i
+// back to back, the heavier first, so every work-group does about the same
+// work (a query tile with key tiles, or a key tile with query tiles) and the
+// last wave of work-groups is not a tail of short ones.  It halves the
+// work-groups, so it is taken only where the queries' own triangle dominates
+// (at most as many earlier keys as queries) and the paired grid still covers
+// every compute unit four times over.  `heads` (batch, head) pairs of
+// `n_tiles` tiles each, where `nq` queries see `nkv` keys.
+inline int pair_causal_grid(int causal, int64_t heads, int n_tiles, int nq, int nkv) {
+  const int64_t paired = heads * ((n_tiles + 1) / 2);
+  return (causal && n_tiles > 1 && nkv - nq <= nq && paired >= 4 * (int64_t)cu_count()) ? 1 : 0;
+}
+
+// The rule for a forward launch (needs p.n_qtiles).
+inline int pair_causal_tiles(const FwdParams& p) {
+  return pair_causal_grid(p.causal, (int64_t)p.n_splits * p.B * p.Hq, p.n_qtiles, p.Nq, p.Nkv);
+}
+
+// Work-group slots per (split, batch, query head): query tiles or pairs.
+__host__ __device__ inline int qtile_slots(const FwdParams& p) {
+  return p.pair_causal ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+}
 
 // Launcher for the tiled kernel (D <= 256) of element type `elt`
 // (attn::Elt) and head dim D, or nullptr if that pair is not instantiated.
@@ -137,6 +180,9 @@ struct BwdParams {
   int group;
   int causal;
   float scale;
+  // causal key tiles of the dK/dV kernel paired first with last in one
+  // work-group (set by the launcher)
+  int pair_kv;
 };
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);

@@ -1,0 +1,116 @@
+"""GPU parity where the launchers pair causal tiles first with last (the ZYFA
+article, "The details that make it production-grade": work-group i of a head
+runs tiles i and n-1-i).
+
+The launchers pair only grids that keep at least four work-groups per compute
+unit after pairing, so these shapes are large: 64 query heads of 3850 rows
+against 3900 keys (31 tiles of 128 rows or keys per head, 16 work-groups per
+head after pairing).  The tile count is odd (the middle tile runs alone), the
+last tile is ragged, and the queries sit 50 keys from the start (causal,
+bottom-right: key j is visible to query i iff j <= i + 50).  Covered: the
+direct-to-LDS bf16 forward (D = 128 and 64), the e4m3-probability forward
+(exact and Lean codes) and the backward's dK/dV kernel.  Every element of
+three heads (the first, the last and the middle one) against the oracle, at
+the bars of the other parity tests: bf16 O within 2e-2 (the forward), LSE
+within 1e-3 x max(1, |LSE|), gradients within 2e-2 of their largest
+magnitude, e4m3-P O within 2e-2 x max(1, |O|) against the float32-decision
+form of the oracle on the "narrow" codes.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_attn_amd import attn as A
+from exact_io_aware_attn_amd.inputs import Workload, make_grad, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+NQ, NKV = 3850, 3900
+HEADS = (0, 31, 63)
+TOL = 2e-2
+TOL_LSE = 1e-3
+LOG2E32 = np.float32(1.4426950408889634)
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def check_lse(L, Lref):
+    fin = np.isfinite(Lref)
+    assert np.array_equal(np.isneginf(L), ~fin), "LSE -inf pattern differs"
+    lerr = (np.abs(L[fin] - Lref[fin]) / np.maximum(1.0, np.abs(Lref[fin]))).max()
+    assert lerr <= TOL_LSE, f"LSE rel err {lerr:.3e}"
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_paired_bf16_forward(D):
+    w = Workload("paired", 1, 64, 16, NQ, NKV, D, True, "bf16", seed=21)
+    note(f"bf16 forward, paired causal tiles, Hq=64 Hkv=16 Nq={NQ} Nkv={NKV} D={D}")
+    q, k, v = make_inputs(w)
+    O, L = A.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.isfinite(O).all()
+    G = w.Hq // w.Hkv
+    worst = 0.0
+    for h in HEADS:
+        Oref, Lref = oracle.attention_head(*(t[0, x].to(torch.float64).numpy() for t, x in
+                                             ((q, h), (k, h // G), (v, h // G))), w.scale, True)
+        err = float(np.abs(O[0, h] - Oref).max())
+        assert err <= TOL, f"head {h}: max |dO| = {err:.3e}"
+        check_lse(L[0, h], Lref)
+        worst = max(worst, err)
+    note(f"  worst max |dO| = {worst:.3e}")
+
+
+@pytest.mark.parametrize("lean", [False, True], ids=["exact", "lean"])
+def test_paired_fp8p_forward(lean):
+    w = Workload("paired8", 1, 64, 16, NQ, NKV, 128, True, "fp8", seed=22, extra={"qk_codes": "narrow"})
+    note(f"e4m3-P forward lean={lean}, paired causal tiles, Hq=64 Hkv=16 Nq={NQ} Nkv={NKV}")
+    q8, k8, v8, desc = make_inputs(w)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda:0") for d in desc]
+    O, L = A.fwd_fp8_p(q8.cuda(), k8.cuda(), v8.cuda(), *ds, causal=True, scale=w.scale, lean=lean)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.isfinite(O).all()
+    # the device's base-2 multiplier: ((scale * log2 e) * dq) * dk in float32
+    c32 = np.float32(np.float32(np.float32(w.scale) * LOG2E32) * desc[0]) * desc[1]
+    G = w.Hq // w.Hkv
+    worst = 0.0
+    for h in HEADS:
+        qv = oracle.e4m3fn_decode(q8[0, h].view(torch.uint8).numpy())
+        kv = oracle.e4m3fn_decode(k8[0, h // G].view(torch.uint8).numpy())
+        vv = oracle.e4m3fn_decode(v8[0, h // G].view(torch.uint8).numpy()) * np.float64(desc[2])
+        Oref, Lref = oracle.fp8p_attention_head_f32(qv, kv, vv, c32, True, lean=lean)
+        ex = float((np.abs(O[0, h] - Oref) / np.maximum(1.0, np.abs(Oref))).max())
+        assert ex <= TOL, f"head {h}: max |dO| / max(1, |O|) = {ex:.3e}"
+        check_lse(L[0, h], Lref)
+        worst = max(worst, ex)
+    note(f"  worst max |dO| / max(1, |O|) = {worst:.3e}")
+
+
+def test_paired_backward():
+    w = Workload("pairedb", 1, 64, 64, NQ, NKV, 128, True, "bf16", seed=23)
+    note(f"backward, paired causal key tiles, Hq=Hkv=64 Nq={NQ} Nkv={NKV} D=128")
+    q, k, v = make_inputs(w)
+    g = make_grad(w)
+    dev = [t.cuda() for t in (q, k, v, g)]
+    O, L = A.fwd(dev[0], dev[1], dev[2], causal=True, scale=w.scale)
+    dq, dk, dv = A.bwd(dev[0], dev[1], dev[2], O, L, dev[3], causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.float().cpu().numpy() for t in (dq, dk, dv))
+    worst = 0.0
+    for h in HEADS:
+        refs = oracle.attention_backward_head(*(t[0, h].to(torch.float64).numpy() for t in (q, k, v, g)),
+                                              scale=w.scale, causal=True)
+        for name, x, r in zip(("dQ", "dK", "dV"), (dq[0, h], dk[0, h], dv[0, h]), refs):
+            err = float(np.abs(x - r).max()) / float(np.abs(r).max())
+            assert err <= TOL, f"head {h} {name}: {err:.3e}"
+            worst = max(worst, err)
+    note(f"  worst max |err| / max |ref| = {worst:.3e}")
