@@ -61,31 +61,31 @@ INPUTS = {
 # workload.  Each entry is tied to a hash of the sources of that kernel;
 # when they have changed since the counters were taken, traffic is null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_io_aware_attn_amd", "csrc")
+# sources of the direct-to-LDS and e4m3-probability kernels (the launch
+# rules, causal tile pairing included, live in attn_launch.h)
+_PIPE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_pipe.hip")
+_P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
-                            200581.4375 * 2 * 1024, 133139.0625 * 1024),
-    "fp8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
-                    188231.9375 * 2 * 1024, 99840.0 * 1024),
+    "prefill_causal_bf16": (_PIPE, "1397d23c8390a197", 267465.4375 * 2 * 1024, 133340.453125 * 1024),
+    "gqa_causal_bf16": (_PIPE, "1397d23c8390a197", 193575.28125 * 2 * 1024, 133120.0 * 1024),
+    "fp8_outlier": (_PIPE, "1397d23c8390a197", 190716.09375 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
-    # write each byte once: 49201 KiB fetched, 49344 KiB written per call)
-    "fp8_blocks_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
-                           189063.1875 * 2 * 1024, 99840.0 * 1024),
+    # write each byte once)
+    "fp8_blocks_outlier": (_PIPE, "1397d23c8390a197", 190768.25 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "b1a4527d429ab446",
                           164165.5 * 2 * 1024, 65664.0 * 1024),
     "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
-    # it reads 16928 KiB x 2 and writes 2080 KiB)
-    "chunk_prefill_splitkv_bf16": (("attn_common.h", "attn_dma.h", "attn_fwd_pipe.hip"), "0e867dd2261e3781",
-                                   73790.0 * 2 * 1024, 33024.0 * 1024),
+    # it reads and writes its parts once)
+    "chunk_prefill_splitkv_bf16": (_PIPE, "1397d23c8390a197", 73792.0 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
-    "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_bwd.hip"), "be68a3764dc561f0",
-                        (133131.0 + 264286.0 + 266836.90625) * 2 * 1024, (4096.0 + 262144.125 + 131082.421875) * 1024),
-    "fp8_p8_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_p8.hip"), "659f97eb1470c201",
-                       189136.9375 * 2 * 1024, 99840.0 * 1024),
-    "fp8_lean_outlier": (("attn_common.h", "attn_dma.h", "attn_fwd_p8.hip"), "659f97eb1470c201",
-                         172636.40625 * 2 * 1024, 99840.0 * 1024),
+    "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.hip"), "62725cf06fe17335",
+                        667898.9375 * 2 * 1024, 397492.28125 * 1024),
+    "fp8_p8_outlier": (_P8, "b5aaae03cea429a6", 188000.03125 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_outlier": (_P8, "b5aaae03cea429a6", 164537.03125 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_causal_32k": (_P8, "b5aaae03cea429a6", 564886.03125 * 2 * 1024, 266241.5 * 1024),
 }
 
 

@@ -24,7 +24,7 @@ import pytest
 from exact_io_aware_attn_amd import build as B
 
 KERNEL_SOURCES = ("attn_fwd_pipe.hip", "attn_fwd_wide.hip", "attn_fwd_splitd.hip", "attn_fwd_tiled.hip",
-                  "attn_merge.hip", "attn_quant.hip", "attn_bwd.hip")
+                  "attn_merge.hip", "attn_quant.hip", "attn_bwd.hip", "attn_fwd_p8.hip")
 
 # kernels allowed a small spill: (source, kernel name fragment) -> max bytes
 # (Q takes D/8 or D/4 VGPRs and O every accumulation register at these D)
