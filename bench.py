@@ -67,25 +67,25 @@ _PIPE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_pipe.hip")
 _P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (_PIPE, "1397d23c8390a197", 267465.4375 * 2 * 1024, 133340.453125 * 1024),
-    "gqa_causal_bf16": (_PIPE, "1397d23c8390a197", 193575.28125 * 2 * 1024, 133120.0 * 1024),
-    "fp8_outlier": (_PIPE, "1397d23c8390a197", 190716.09375 * 2 * 1024, 99840.0 * 1024),
+    "prefill_causal_bf16": (_PIPE, "9625496cc54dc57a", 267065.53125 * 2 * 1024, 133138.328125 * 1024),
+    "gqa_causal_bf16": (_PIPE, "9625496cc54dc57a", 194269.6875 * 2 * 1024, 133120.0 * 1024),
+    "fp8_outlier": (_PIPE, "9625496cc54dc57a", 190049.375 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
-    "fp8_blocks_outlier": (_PIPE, "1397d23c8390a197", 190768.25 * 2 * 1024, 99840.0 * 1024),
+    "fp8_blocks_outlier": (_PIPE, "9625496cc54dc57a", 187709.25 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "b1a4527d429ab446",
                           164165.5 * 2 * 1024, 65664.0 * 1024),
     "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
-    "chunk_prefill_splitkv_bf16": (_PIPE, "1397d23c8390a197", 73792.0 * 2 * 1024, 33024.0 * 1024),
+    "chunk_prefill_splitkv_bf16": (_PIPE, "9625496cc54dc57a", 73785.5 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
     "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.hip"), "62725cf06fe17335",
                         667898.9375 * 2 * 1024, 397492.28125 * 1024),
-    "fp8_p8_outlier": (_P8, "b5aaae03cea429a6", 188000.03125 * 2 * 1024, 99840.0 * 1024),
-    "fp8_lean_outlier": (_P8, "b5aaae03cea429a6", 164537.03125 * 2 * 1024, 99840.0 * 1024),
-    "fp8_lean_causal_32k": (_P8, "b5aaae03cea429a6", 564886.03125 * 2 * 1024, 266241.5 * 1024),
+    "fp8_p8_outlier": (_P8, "8da976182d1602e4", 172394.375 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_outlier": (_P8, "8da976182d1602e4", 123132.03125 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_causal_32k": (_P8, "8da976182d1602e4", 473900.53125 * 2 * 1024, 266242.203125 * 1024),
 }
 
 

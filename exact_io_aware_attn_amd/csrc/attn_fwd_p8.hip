@@ -193,6 +193,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_p8_kernel(FwdParams p) {
     if (kt + 1 < n_kt) issue(kt + 1, slot ^ 1);
     const char* const kb_cur = lds + slot * C::SLOT;
     const char* const vb_cur = kb_cur + C::TILE;
+    // a causal tile entirely above this wave's rows (loaded for the
+    // work-group's later waves) adds nothing to them
+    if (p.causal && kt * C::BC > q0w + 31 + kr.kv_off) continue;
 
     // ---- S^T = K Q^T ------------------------------------------------------
     f32x16 s[2];

@@ -361,6 +361,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 128) ? 2 : 1) void attn_f
     const char* const kb_cur = lds + slot * C::TILE_K;
     const char* const vb_cur = ldsV + slot * C::TILE;
     slot = slot == NBUF - 1 ? 0 : slot + 1;
+    // a causal tile entirely above this wave's rows (loaded for the
+    // work-group's later waves) adds nothing to them
+    if (p.causal && kt * C::BC > q0w + C::QW - 1 + kr.kv_off) continue;
 
   // ---- S^T = K Q^T ------------------------------------------------------------
     f32x16 s[QB][C::NKB];
