@@ -8,8 +8,9 @@ against 3900 keys (31 tiles of 128 rows or keys per head, 16 work-groups per
 head after pairing).  The tile count is odd (the middle tile runs alone), the
 last tile is ragged, and the queries sit 50 keys from the start (causal,
 bottom-right: key j is visible to query i iff j <= i + 50).  Covered: the
-direct-to-LDS bf16 forward (D = 128 and 64), the e4m3-probability forward
-(exact and Lean codes) and the backward's dK/dV kernel.  Every element of
+direct-to-LDS bf16 forward (D = 128 and 64; also split into four key ranges
+and merged), the e4m3-probability forward (exact and Lean codes) and the
+backward's dK/dV kernel.  Every element of
 three heads (the first, the last and the middle one) against the oracle, at
 the bars of the other parity tests: bf16 O within 2e-2 (the forward), LSE
 within 1e-3 x max(1, |LSE|), gradients within 2e-2 of their largest
@@ -114,3 +115,26 @@ def test_paired_backward():
             assert err <= TOL, f"head {h} {name}: {err:.3e}"
             worst = max(worst, err)
     note(f"  worst max |err| / max |ref| = {worst:.3e}")
+
+
+def test_paired_splitkv_forward():
+    """Pairing inside each key range of a split launch (4 ranges, 32 query
+    heads: 2048 work-groups after pairing), then the LSE merge."""
+    w = Workload("pairedskv", 1, 32, 8, NQ, NKV, 128, True, "bf16", seed=24)
+    note(f"bf16 split-KV forward (4 ranges), paired causal tiles, Hq=32 Hkv=8 Nq={NQ} Nkv={NKV}")
+    q, k, v = make_inputs(w)
+    O, L = A.fwd_splitkv(q.cuda(), k.cuda(), v.cuda(), 4, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.isfinite(O).all()
+    G = w.Hq // w.Hkv
+    worst = 0.0
+    for h in (0, 15, 31):
+        Oref, Lref = oracle.attention_head(*(t[0, x].to(torch.float64).numpy() for t, x in
+                                             ((q, h), (k, h // G), (v, h // G))), w.scale, True)
+        err = float(np.abs(O[0, h] - Oref).max())
+        assert err <= TOL, f"head {h}: max |dO| = {err:.3e}"
+        check_lse(L[0, h], Lref)
+        worst = max(worst, err)
+    note(f"  worst max |dO| = {worst:.3e}")
