@@ -67,19 +67,19 @@ _PIPE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_pipe.hip")
 _P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (_PIPE, "9625496cc54dc57a", 267065.53125 * 2 * 1024, 133138.328125 * 1024),
-    "gqa_causal_bf16": (_PIPE, "9625496cc54dc57a", 194269.6875 * 2 * 1024, 133120.0 * 1024),
-    "fp8_outlier": (_PIPE, "9625496cc54dc57a", 190049.375 * 2 * 1024, 99840.0 * 1024),
+    "prefill_causal_bf16": (_PIPE, "e207c00edc922816", 271829.46875 * 2 * 1024, 133294.953125 * 1024),
+    "gqa_causal_bf16": (_PIPE, "e207c00edc922816", 196709.40625 * 2 * 1024, 133120.171875 * 1024),
+    "fp8_outlier": (_PIPE, "e207c00edc922816", 189905.09375 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
-    "fp8_blocks_outlier": (_PIPE, "9625496cc54dc57a", 187709.25 * 2 * 1024, 99840.0 * 1024),
+    "fp8_blocks_outlier": (_PIPE, "e207c00edc922816", 187838.71875 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "b1a4527d429ab446",
                           164165.5 * 2 * 1024, 65664.0 * 1024),
     "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
-    "chunk_prefill_splitkv_bf16": (_PIPE, "9625496cc54dc57a", 73785.5 * 2 * 1024, 33024.0 * 1024),
+    "chunk_prefill_splitkv_bf16": (_PIPE, "e207c00edc922816", 73783.5 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
     "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.hip"), "62725cf06fe17335",
                         667898.9375 * 2 * 1024, 397492.28125 * 1024),

@@ -1,6 +1,7 @@
-"""GPU parity where the launchers pair causal tiles first with last (the ZYFA
-article, "The details that make it production-grade": work-group i of a head
-runs tiles i and n-1-i).
+"""GPU parity on grids large enough for the launchers' large-grid choices:
+causal tiles paired first with last (the ZYFA article, "The details that make
+it production-grade": work-group i of a head runs tiles i and n-1-i), and, for
+bf16 D = 128, 32-key tiles at three waves per SIMD.
 
 The launchers pair only grids that keep at least four work-groups per compute
 unit after pairing, so these shapes are large: 64 query heads of 3850 rows
@@ -133,6 +134,31 @@ def test_paired_splitkv_forward():
     for h in (0, 15, 31):
         Oref, Lref = oracle.attention_head(*(t[0, x].to(torch.float64).numpy() for t, x in
                                              ((q, h), (k, h // G), (v, h // G))), w.scale, True)
+        err = float(np.abs(O[0, h] - Oref).max())
+        assert err <= TOL, f"head {h}: max |dO| = {err:.3e}"
+        check_lse(L[0, h], Lref)
+        worst = max(worst, err)
+    note(f"  worst max |dO| = {worst:.3e}")
+
+
+def test_large_grid_noncausal_ragged():
+    """The bf16 D = 128 launcher picks 32-key tiles at three waves per SIMD
+    when the grid gives every CU three work-groups (64 heads x 31 query tiles
+    here, non-causal, ragged query and key tails); smaller grids run 64-key
+    tiles, which the small-shape parity tests cover."""
+    w = Workload("largegrid", 1, 64, 16, NQ, NKV, 128, False, "bf16", seed=25)
+    note(f"bf16 non-causal forward, large grid, Hq=64 Hkv=16 Nq={NQ} Nkv={NKV}")
+    q, k, v = make_inputs(w)
+    O, L = A.fwd(q.cuda(), k.cuda(), v.cuda(), causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.isfinite(O).all()
+    G = w.Hq // w.Hkv
+    worst = 0.0
+    for h in HEADS:
+        Oref, Lref = oracle.attention_head(*(t[0, x].to(torch.float64).numpy() for t, x in
+                                             ((q, h), (k, h // G), (v, h // G))), w.scale, False)
         err = float(np.abs(O[0, h] - Oref).max())
         assert err <= TOL, f"head {h}: max |dO| = {err:.3e}"
         check_lse(L[0, h], Lref)
