@@ -8,12 +8,16 @@ JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Without --warmup/--steps the counts are sized from a short probe so that the
-untimed warm-up lasts about 1.5 s and the timed loop about 1 s: under
-sustained load the GPU settles at a lower clock than in the first tens of
-milliseconds, and the timed steps should see the settled clock (the ZYFA
-article, "What the numbers establish, and where they overstate", makes the
-same point about sustained clocks).
+The untimed warm-up lasts at least --warmup steps and at least about 1.5 s
+of back-to-back work (the given count is a minimum): a GPU coming out of idle
+first runs below, then above, the clock it settles at under sustained load,
+and the timed steps should see the settled clock (the ZYFA article, "What the
+numbers establish, and where they overstate", makes the same point about
+sustained clocks).  Exactly --steps steps are timed (without --steps: about
+1 s of work).  The shader clock is sampled through amdsmi during the last
+part of the warm-up and the timed loop; the JSON line reports it, the
+percentage of the peak normalised to it, and the median, best, first and last
+per-launch times.
 
 Throughput is matmul TFLOP/s: 4 * B * Hq * D * (visible query/key pairs) per
 step (the QK^T and PV products; softmax work is not counted).  The roofline
@@ -43,11 +47,15 @@ METRIC = "attention fwd TFLOPS on 1 MI355X and % of dense bf16/fp8 MFMA peak"
 METRIC_BWD = "attention bwd TFLOPS on 1 MI355X (5 matmuls counted) and % of dense bf16 MFMA peak"
 # MI355X dense MFMA peaks (TFLOP/s): bf16 2.5 PF, fp8 5.0 PF, fp32 157.3 TF.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
-DEFAULT_WORKLOAD = "prefill_causal_bf16"
-# The pages' own MI355X figure for a workload (TFLOP/s): the ZYFA article,
-# "What the numbers establish, and where they overstate": 2672 TFLOP/s for
-# fp8 causal prefill at 32K tokens, D = 128, Gaussian inputs.
-BASELINE_TFLOPS = {"fp8_p8_causal_32k": 2672.0, "fp8_lean_causal_32k": 2672.0}
+# the gated configuration: GQA causal prefill, B2 Hq32 Hkv8 N8192 D128, bf16
+DEFAULT_WORKLOAD = "gqa_causal_bf16"
+# datasheet clock of the dense peaks above (MHz)
+PEAK_SCLK_MHZ = 2400.0
+# The pages' MI355X figure closest to a workload (TFLOP/s), reported as
+# context only: the ZYFA article, "What the numbers establish, and where they
+# overstate", gives 2672 TFLOP/s for its own fp8 kernel on causal prefill at
+# 32K tokens, D = 128, Gaussian inputs, with an unstated head count.
+CONTEXT_TFLOPS = {"fp8_p8_causal_32k": 2672.0, "fp8_lean_causal_32k": 2672.0}
 INPUTS = {
     "fp8": "i.i.d. N(0,1), 1% outlier channels x8, per-tensor e4m3, seed 0",
     "fp8blk": "bf16 i.i.d. N(0,1), 1% outlier channels x8 shared by Q and K, seed 0; "
@@ -102,13 +110,108 @@ def measured_traffic(name):
     return int(round(rd + wr)) if m.hexdigest()[:16] == digest else None
 
 
+class ClockSampler:
+    """Samples the GPU's current shader (gfx) clock in a background thread
+    through amdsmi, every `period` seconds, between start() and stop().
+    Reports nothing (None) where amdsmi or the metric is unavailable."""
+
+    def __init__(self, period=0.01, enabled=True):
+        import threading
+        self.period = period
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._smi = None
+        if not enabled:
+            self.error = "not sampled (--no-sclk)"
+            return
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._handle = handles[0] if handles else None
+            self._smi = amdsmi
+        except Exception as e:  # pragma: no cover - depends on the machine
+            self.error = f"amdsmi unavailable: {type(e).__name__}"
+
+    def _read(self):
+        smi = self._smi
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(self._handle)
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            if clks:
+                return float(np.mean(clks))
+            c = m.get("current_gfxclk")
+            if isinstance(c, (int, float)) and 0 < c < 10000:
+                return float(c)
+        except Exception:
+            pass
+        info = smi.amdsmi_get_clock_info(self._handle, smi.AmdSmiClkType.GFX)
+        c = info.get("clk")
+        return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                c = self._read()
+                if c is not None:
+                    self.samples.append(c)
+            except Exception as e:  # pragma: no cover
+                self.error = f"amdsmi read failed: {type(e).__name__}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._smi is None or self._handle is None:
+            return
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:  # pragma: no cover
+                pass
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = np.asarray(self.samples)
+        return {"median_mhz": round(float(np.median(s)), 1), "min_mhz": round(float(s.min()), 1),
+                "max_mhz": round(float(s.max()), 1), "samples": int(s.size),
+                "source": "amdsmi current gfx clock (mean over XCDs), sampled every 10 ms over the last "
+                          "0.5 s of warm-up and the timed loop"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 1 s of work)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: about 1.5 s of work)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="minimum untimed steps (the warm-up also lasts at least about 1.5 s)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="minimum duration of the warm-up (0 for counter-collection runs)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true", help="do not sample the shader clock (profiler runs)")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0 = time budget)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -281,6 +384,8 @@ def cpu_baseline(w, host_inp, n_heads, seconds):
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name} (drawn at random, seed 1), fp64 numpy, "
                   f"S materialised per head; {dt:.1f} s wall, scaled by the same flop formula",
+        "cpu_model": cpu_model(),
+        "os_cpu_count": os.cpu_count(),
     }
 
 
@@ -307,22 +412,27 @@ def main():
 
     # size the warm-up and the timed loop from a short probe (its steps count
     # as warm-up steps)
-    probe = 10 if args.warmup is None else min(10, args.warmup)
+    probe = 10 if args.warmup is None else max(1, min(10, args.warmup))
     torch.cuda.synchronize()
     t_probe = time.perf_counter()
     for _ in range(probe):
         step()
     torch.cuda.synchronize()
-    est = max((time.perf_counter() - t_probe) / max(probe, 1), 1e-6)
-    if args.warmup is None:
-        args.warmup = int(min(20000, max(50, math.ceil(1.5 / est))))
+    est = max((time.perf_counter() - t_probe) / probe, 1e-6)
+    floor = int(min(20000, max(50, math.ceil(args.warmup_seconds / est)))) if args.warmup_seconds > 0 else 0
+    warmup = max(args.warmup or 0, floor, probe)
     if args.steps is None:
         args.steps = int(min(5000, max(200, math.ceil(1.0 / est))))
-    for _ in range(max(0, args.warmup - probe)):
+    # the clock is sampled over the last ~0.5 s of the warm-up and the timed loop
+    tail = max(0, min(warmup - probe, int(math.ceil(0.5 / est))))
+    for _ in range(max(0, warmup - probe - tail)):
+        step()
+    clock = ClockSampler(enabled=not args.no_sclk)
+    clock.start()
+    for _ in range(max(0, tail)):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -330,7 +440,8 @@ def main():
         step(pair)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in ev]
+    clock.stop()
+    kernel_ms = np.asarray([s.elapsed_time(e) for s, e in ev])
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
 
     ms_per_step = wall * 1e3 / args.steps
@@ -339,17 +450,18 @@ def main():
     achieved = flops / avg_kernel_s / 1e12
     compute_dtype = "fp8" if w.dtype == "fp8blk" else w.dtype
     peak = PEAK_TFLOPS[compute_dtype]
+    sclk = clock.summary()
     res = {
         "metric": METRIC_BWD if is_bwd(w) else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / BASELINE_TFLOPS[w.name], 4) if w.name in BASELINE_TFLOPS else None,
+        "vs_baseline": None,
         "dtype": compute_dtype,
         "data": "synthetic",
         "config": {
@@ -379,7 +491,20 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(w.name),
+            "frac_at_measured_sclk": (round(achieved / (peak * sclk["median_mhz"] / PEAK_SCLK_MHZ), 4)
+                                      if sclk else None),
         },
+        "sclk": sclk if sclk else {"median_mhz": None, "note": clock.error or "no samples"},
+        "kernel_ms": {
+            "mean": round(float(kernel_ms.mean()), 5),
+            "median": round(float(np.median(kernel_ms)), 5),
+            "min": round(float(kernel_ms.min()), 5),
+            "first": round(float(kernel_ms[0]), 5),
+            "last": round(float(kernel_ms[-1]), 5),
+            "what": "HIP events on the launch stream around the dominant kernel of each timed step",
+        },
+        "context_tflops": ({"value": CONTEXT_TFLOPS[w.name], "source": "ZYFA article, own fp8 kernel, other "
+                           "head count: context, not a baseline"} if w.name in CONTEXT_TFLOPS else None),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -111,6 +111,37 @@ def _shapes(q, k, v):
     return B, Hq, Hkv, Nq, Nkv, D
 
 
+def _buffer(t, name, shape, dtype, device):
+    """A caller-supplied output buffer, checked before any kernel writes it:
+    exactly ``shape`` and ``dtype``, contiguous, on ``device``.  ``None``
+    allocates one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(ws, need, device):
+    """A caller-supplied workspace of at least ``need`` bytes on ``device``
+    (contiguous), or a new one."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
+
+
 def _stream_ptr(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -134,10 +165,9 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True, 
         raise ValueError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buffer(out, "out", (B, Hq, Nq, D), q.dtype, q.device)
+    if lse is not None or return_lse:
+        lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(raw_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                    lse.data_ptr() if lse is not None else None,
                    B, Hq, Hkv, Nq, Nkv, D, causal, scale, dt, _stream_ptr(stream)))
@@ -165,10 +195,9 @@ def fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=Fals
         ptrs.append(d.data_ptr())
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buffer(out, "out", (B, Hq, Nq, D), torch.bfloat16, q.device)
+    if lse is not None or return_lse:
+        lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(raw_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                        lse.data_ptr() if lse is not None else None,
                        B, Hq, Hkv, Nq, Nkv, D, causal, scale, *ptrs, _stream_ptr(stream)))
@@ -260,15 +289,13 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, work
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = splitkv_workspace_bytes(B, Hq, Nq, D, n_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = out if out is not None else torch.empty((B, Hq, Nq, D), dtype=torch.float32 if dt == ATTN_F32 else
-                                                torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
+    o = _buffer(out, "out", (B, Hq, Nq, D), torch.float32 if dt == ATTN_F32 else torch.bfloat16, q.device)
+    lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, *dptr, int(n_splits),
-                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(stream)))
     return o, lse
 
 
@@ -285,14 +312,8 @@ def quantize_fp8(x, signs=None, codes=None, descales=None, stream=None):
         if signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != D:
             raise ValueError("signs must be an int8 device tensor of D values")
         sp = signs.data_ptr()
-    if codes is None:
-        codes = torch.empty((B, H, N, D), dtype=torch.float8_e4m3fn, device=x.device)
-    if descales is None:
-        descales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
-    if codes.dtype != torch.float8_e4m3fn or tuple(codes.shape) != (B, H, N, D) or not codes.is_contiguous():
-        raise ValueError("codes must be a contiguous float8_e4m3fn tensor of x's shape")
-    if descales.dtype != torch.float32 or tuple(descales.shape) != (B, H, (N + 63) // 64):
-        raise ValueError("descales must be float32 of shape (B, H, ceil(N/64))")
+    codes = _buffer(codes, "codes", (B, H, N, D), torch.float8_e4m3fn, x.device)
+    descales = _buffer(descales, "descales", (B, H, (N + 63) // 64), torch.float32, x.device)
     desc = descales
     _check(lib().attn_quantize_fp8(x.data_ptr(), codes.data_ptr(), desc.data_ptr(), B, H, N, D, sp,
                                    _stream_ptr(stream)))
@@ -312,10 +333,9 @@ def fwd_fp8_blocks(q, k, v, dq_blocks, dk_blocks, dv_blocks, causal=False, scale
             raise ValueError("block descales must be float32 device tensors of shape (B, H, ceil(N/64))")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buffer(out, "out", (B, Hq, Nq, D), torch.bfloat16, q.device)
+    if lse is not None or return_lse:
+        lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(lib().attn_fwd_fp8_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D,
                                      int(causal), float(scale), dq_blocks.data_ptr(), dk_blocks.data_ptr(),
@@ -340,12 +360,14 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, dq=None
         raise ValueError("lse must be a contiguous float32 (B, Hq, Nq) tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    for t in (o, lse, dout):
+        if t.device != q.device:
+            raise ValueError("o, lse and dout must be on q's device")
     need = bwd_workspace_bytes(B, Hq, Nq)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    workspace = _workspace(workspace, need, q.device)
+    dq = _buffer(dq, "dq", tuple(q.shape), torch.bfloat16, q.device)
+    dk = _buffer(dk, "dk", tuple(k.shape), torch.bfloat16, q.device)
+    dv = _buffer(dv, "dv", tuple(v.shape), torch.bfloat16, q.device)
     _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, int(causal),
                           float(scale), ATTN_BF16, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -371,10 +393,9 @@ def fwd_fp8_p(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal=Fa
         ptrs.append(d.data_ptr())
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buffer(out, "out", (B, Hq, Nq, D), torch.bfloat16, q.device)
+    if lse is not None or return_lse:
+        lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(lib().attn_fwd_fp8_p(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, int(causal),
                                 float(scale), *ptrs, ATTN_P_E4M3_LEAN if lean else ATTN_P_E4M3, _stream_ptr(stream)))
@@ -390,10 +411,9 @@ def fwd_exp_poly(q, k, v, causal=False, scale=None, out=None, lse=None, return_l
             raise ValueError("fwd_exp_poly takes bfloat16 tensors")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = _buffer(out, "out", (B, Hq, Nq, D), torch.bfloat16, q.device)
+    if lse is not None or return_lse:
+        lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     _check(lib().attn_fwd_exp_poly(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, int(causal),
                                    float(scale), _stream_ptr(stream)))

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -142,6 +143,65 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   p.blk_scaled = blk_scaled ? 1 : 0;
   hipError_t err = fn(p, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+// Checks of attn_fwd_splitkv's arguments that do not involve the workspace
+// (the rest are run_forward's).
+int splitkv_check(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t Hq, int64_t Hkv,
+                  int64_t Nq, int64_t Nkv, int64_t D, float scale, int dtype, const float* descale_q,
+                  const float* descale_k, const float* descale_v, int64_t n_splits) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL device pointers");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (Hkv < 1 || (Hq >= 1 && Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID_ARG, "Hkv must be >= 1 and divide Hq");
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dtype != ATTN_FP8_E4M3 && (descale_q || descale_k || descale_v))
+    return fail(ATTN_ERR_INVALID_ARG, "descales apply to ATTN_FP8_E4M3 only");
+  if (n_splits < 1 || n_splits > 4096) return fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [1, 4096]");
+  if (B < 1 || Hq < 1 || Nq < 1 || Nkv < 1 || D < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1");
+  return ATTN_OK;
+}
+
+// The partial-attention launch over n_splits key ranges into `workspace`
+// (attn_splitkv_workspace_bytes of it: float32 partial O of every split, then
+// float32 partial LSE of every split, each part 256-byte aligned), then the
+// merge into o and lse.  Every element of the partial results is written by
+// the first launch before the second reads it (a range without keys for a
+// row writes O = 0, LSE = -inf), so the workspace needs no clearing.
+int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale, int dtype,
+                const float* descale_q, const float* descale_k, const float* descale_v, int64_t n_splits,
+                void* workspace, attn_stream_t stream) {
+  const int64_t rows = B * Hq * Nq;
+  const int64_t o_bytes = (rows * D * 4 + 255) / 256 * 256;
+  const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + n_splits * o_bytes);
+  // ranges of a multiple of 64 keys (whole tiles of every kernel); trailing
+  // ranges may be short or empty
+  const int64_t split_len = ((Nkv + n_splits - 1) / n_splits + 63) / 64 * 64;
+  const Ranges r{0, Nkv, split_len, n_splits, true, o_bytes / 4, l_bytes / 4};
+  int st = run_forward(q, k, v, o_parts, lse_parts, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q,
+                       descale_k, descale_v, &r, stream);
+  if (st != ATTN_OK) return st;
+  attn::MergeParams mp{};
+  mp.o_parts = o_parts;
+  mp.lse_parts = lse_parts;
+  mp.o = o;
+  mp.lse = lse;
+  mp.n_parts = (int)n_splits;
+  mp.D = (int)D;
+  mp.o_f32 = dtype == ATTN_F32 ? 1 : 0;
+  mp.rows = rows;
+  mp.o_part_stride = o_bytes / 4;
+  mp.lse_part_stride = l_bytes / 4;
+  hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
   return ATTN_OK;
 }
 
@@ -342,41 +402,15 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      const float* descale_q, const float* descale_k, const float* descale_v, int64_t n_splits,
                      void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   g_last_error[0] = '\0';
-  if (dtype != ATTN_FP8_E4M3 && (descale_q || descale_k || descale_v))
-    return fail(ATTN_ERR_INVALID_ARG, "descales apply to ATTN_FP8_E4M3 only");
-  if (n_splits < 1 || n_splits > 4096) return fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [1, 4096]");
-  if (B < 1 || Hq < 1 || Nq < 1 || Nkv < 1 || D < 1)
-    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1");
+  const int st = splitkv_check(q, k, v, o, B, Hq, Hkv, Nq, Nkv, D, scale, dtype, descale_q, descale_k, descale_v,
+                               n_splits);
+  if (st != ATTN_OK) return st;
   const size_t need = attn_splitkv_workspace_bytes(B, Hq, Nq, D, n_splits);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_INVALID_ARG, "workspace must be a device buffer of at least %zu bytes", need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int64_t rows = B * Hq * Nq;
-  const int64_t o_bytes = (rows * D * 4 + 255) / 256 * 256;
-  const int64_t l_bytes = (rows * 4 + 255) / 256 * 256;
-  float* o_parts = static_cast<float*>(workspace);
-  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + n_splits * o_bytes);
-  // ranges of a multiple of 64 keys (whole tiles of every kernel); trailing
-  // ranges may be short or empty
-  const int64_t split_len = ((Nkv + n_splits - 1) / n_splits + 63) / 64 * 64;
-  const Ranges r{0, Nkv, split_len, n_splits, true, o_bytes / 4, l_bytes / 4};
-  int st = run_forward(q, k, v, o_parts, lse_parts, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q,
-                       descale_k, descale_v, &r, stream);
-  if (st != ATTN_OK) return st;
-  attn::MergeParams mp{};
-  mp.o_parts = o_parts;
-  mp.lse_parts = lse_parts;
-  mp.o = o;
-  mp.lse = lse;
-  mp.n_parts = (int)n_splits;
-  mp.D = (int)D;
-  mp.o_f32 = dtype == ATTN_F32 ? 1 : 0;
-  mp.rows = rows;
-  mp.o_part_stride = o_bytes / 4;
-  mp.lse_part_stride = l_bytes / 4;
-  hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
-  return ATTN_OK;
+  return splitkv_run(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q, descale_k, descale_v,
+                     n_splits, workspace, stream);
 }
 
 const char* attn_status_string(int status) {

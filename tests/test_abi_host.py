@@ -214,3 +214,44 @@ def test_bwd_invalid_arguments(kw):
 @pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(dtype=A.ATTN_F32), dict(dtype=A.ATTN_FP8_E4M3)])
 def test_bwd_unsupported(kw):
     assert bwd_call(**kw) == A.ATTN_ERR_UNSUPPORTED
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="a GPU is visible: the call would launch")
+def test_valid_call_without_device_returns_hip_error():
+    # Arguments pass validation, so the call reaches the launch, which fails
+    # without a device: ATTN_ERR_HIP, with the HIP error in the message.
+    st = call(B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, D=128)
+    assert st == A.ATTN_ERR_HIP
+    assert b"launch failed" in A.lib().attn_last_error()
+
+
+def test_binding_output_buffer_checks():
+    import torch
+    dev = torch.device("cpu")
+    shape = (1, 2, 8, 64)
+    good = torch.empty(shape, dtype=torch.bfloat16)
+    assert A._buffer(good, "out", shape, torch.bfloat16, dev) is good
+    assert A._buffer(None, "out", shape, torch.bfloat16, dev).shape == shape
+    with pytest.raises(ValueError, match="shape"):
+        A._buffer(torch.empty((1, 2, 7, 64), dtype=torch.bfloat16), "out", shape, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="dtype"):
+        A._buffer(torch.empty(shape, dtype=torch.float32), "out", shape, torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        A._buffer(torch.empty((1, 2, 64, 8), dtype=torch.bfloat16).transpose(2, 3), "out", shape, torch.bfloat16,
+                  dev)
+    with pytest.raises(ValueError, match="expected meta"):
+        A._buffer(good, "out", shape, torch.bfloat16, torch.device("meta"))
+    ws = torch.empty(100, dtype=torch.uint8)
+    assert A._workspace(ws, 100, dev) is ws
+    with pytest.raises(ValueError, match="needed"):
+        A._workspace(ws, 101, dev)
+    assert A._workspace(torch.empty(30, dtype=torch.float32), 120, dev).numel() == 30
+

@@ -3,15 +3,23 @@ ABI, exact and Lean P codes) against the oracle's ``fp8p_attention`` (the
 ZYFA article's per-block power-of-two scaling with a rounded row sum, and
 Lean P), and its accuracy against exact attention.
 
-Parity: every rounding decision (block exponent, e4m3 code, Lean code) is
-an integer decided from float32 values, so the oracle takes it in float32 as
-the device does (``fp8p_attention_head_f32``), on Q/K codes whose dot
-products are exact in float32 (the "narrow" recipe: magnitudes in [1/2, 4));
-what remains is float32 accumulation in P V and the bf16 rounding of O:
-2e-2 x max(1, |O_ref|) element by element, LSE 1e-3 x max(1, |LSE|).
-On other inputs (outlier channels, Gaussian codes) float32 and float64
-scores round some codes differently, so those are checked for accuracy
-against exact attention instead: the e4m3-P error within e4m3 precision of
+Parity, two ways:
+  * on the real inputs (Gaussian codes with 1% outlier channels, the
+    benchmarked problem at full size on sampled rows): against the float64
+    oracle ``fp8p_attention_head``, boundary-aware (``fp8_bounds``).  Every
+    rounding decision (block exponent, e4m3 code, Lean code) may differ from
+    the oracle's only where the oracle's decision input lies within the
+    device arithmetic's error bound of a decision boundary (the scores come
+    from the fp8 matrix instruction's grouped accumulation, the multiplier
+    and the multiply-add in float32); the admissible deviation of each
+    weight bounds O and LSE row by row, plus the grouped accumulation of
+    P V and of the row sum, and bf16 rounding of O.  LSE also within
+    1e-3 * max(1, |LSE|) plus that bound.
+  * on Q/K codes whose dot products are exact in float32 (the "narrow"
+    recipe: magnitudes in [1/2, 4)), against ``fp8p_attention_head_f32``,
+    which takes every decision in float32 as the device does: 2e-2 x
+    max(1, |O_ref|) element by element, LSE 1e-3 x max(1, |LSE|).
+Accuracy against exact attention: the e4m3-P error within e4m3 precision of
 O's scale, Lean P's error 1-2x it (the article documents 1.22-1.36x).
 """
 import sys
@@ -22,6 +30,7 @@ import torch
 
 import oracle
 from exact_io_aware_attn_amd import attn as A
+from fp8_bounds import fp8p_accumulation_bound, fp8p_row_bounds
 from exact_io_aware_attn_amd.inputs import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -114,29 +123,90 @@ def test_fp8p_accuracy_against_exact():
     assert 1.0 <= el / ee <= 2.0
 
 
+def check_bounded(O, L, qc, kc, v, dq, dk, scale, causal, lean, rows):
+    """Device rows O, L against the float64 oracle within the admissible
+    deviation of the decisions plus the accumulation in P V and the bf16
+    rounding of O.  Returns (worst |dO| / bound, ambiguous fraction)."""
+    Oref, Lref, bO, bL, amb, p = fp8p_row_bounds(qc, kc, v, dq, dk, scale, causal, lean, rows)
+    worst = 0.0
+    fin = np.isfinite(Lref)
+    assert np.array_equal(np.isneginf(L), ~fin), "LSE -inf pattern differs"
+    assert np.isfinite(O).all()
+    for i in range(rows.size):
+        if not fin[i]:
+            assert (O[i] == 0).all()
+            continue
+        accO, accL = fp8p_accumulation_bound(Oref[i], p[i], v)
+        lim = (bO[i] + accO) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Oref[i]) + 1e-7
+        d = np.abs(O[i] - Oref[i])
+        assert (d <= lim).all(), (f"row {rows[i]}: |dO| {d.max():.3e} beyond the admissible "
+                                  f"{lim[int(np.argmax(d - lim))]:.3e}")
+        worst = max(worst, float((d / lim).max()))
+        dl = abs(L[i] - Lref[i])
+        assert dl <= bL[i] + accL + 5e-4, f"row {rows[i]}: |dLSE| {dl:.3e} beyond {bL[i] + accL + 5e-4:.3e}"
+        assert dl <= bL[i] + accL + 1e-3 * max(1.0, abs(Lref[i]))
+    return worst, float(amb.mean())
+
+
+REAL = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal): outlier-channel inputs
+    (1, 2, 2, 300, 700, 128, True),
+    (1, 4, 2, 257, 513, 128, False),
+    (1, 2, 1, 333, 129, 128, True),     # Nq > Nkv: rows without keys
+    (1, 2, 2, 200, 450, 64, False),
+]
+
+
+@pytest.mark.parametrize("lean", [False, True], ids=["exact", "lean"])
+@pytest.mark.parametrize("case", REAL, ids=lambda c: "x".join(map(str, c)))
+def test_fp8p_parity_real_inputs(case, lean):
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    note(f"fwd_fp8_p lean={lean} real inputs {case}")
+    w = Workload("p8real", B, Hq, Hkv, Nq, Nkv, D, causal, "fp8", seed=6, outlier_frac=0.01)
+    q8, k8, v8, desc = make_inputs(w)
+    qc, kc = (oracle.e4m3fn_decode(t.view(torch.uint8).numpy()) for t in (q8, k8))
+    vv = oracle.e4m3fn_decode(v8.view(torch.uint8).numpy()) * np.float64(desc[2])
+    dev = [t.cuda() for t in (q8, k8, v8)]
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda:0") for d in desc]
+    O, L = run(w, dev, ds, lean)
+    G = Hq // Hkv
+    rows = np.arange(Nq)
+    worst, amb = 0.0, []
+    for b in range(B):
+        for h in range(Hq):
+            r, a = check_bounded(O[b, h].astype(np.float64), L[b, h].astype(np.float64), qc[b, h], kc[b, h // G],
+                                 vv[b, h // G], desc[0], desc[1], w.scale, causal, lean, rows)
+            worst, amb = max(worst, r), amb + [a]
+    note(f"  worst |dO| / admissible {worst:.3f}; open decisions {np.mean(amb):.4f}")
+
+
 @pytest.mark.parametrize("lean", [False, True], ids=["exact", "lean"])
 def test_fp8p_full_size_sampled(lean):
-    """The benchmarked problem (24 x 16K x 16K, D = 128, outlier channels):
-    sampled rows against exact attention and against the oracle's e4m3-P
-    result in float64 (RMS over the rows: rounding decisions may differ
-    between float32 and float64 scores, element by element)."""
+    """The benchmarked problem (24 x 16K x 16K, D = 128, outlier channels)
+    in the launch configuration the bench times, on sampled rows: the
+    boundary-aware parity against the float64 oracle, and the accuracy
+    against exact attention."""
     w = WORKLOADS["fp8_outlier"]
     note(f"{w.name} e4m3 P lean={lean}, full size")
-    exact, dev, ds = inputs(w)
+    q8, k8, v8, desc = make_inputs(w)
+    qc, kc = (oracle.e4m3fn_decode(t.view(torch.uint8).numpy()) for t in (q8, k8))
+    vv = oracle.e4m3fn_decode(v8.view(torch.uint8).numpy()) * np.float64(desc[2])
+    dev = [t.cuda() for t in (q8, k8, v8)]
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda:0") for d in desc]
     O, L = run(w, dev, ds, lean)
     assert np.isfinite(O).all() and np.isfinite(L).all()
     rng = np.random.default_rng(3)
-    err_x, err_p, scale = [], [], []
+    err_x, scale, worst, amb = [], [], 0.0, []
     for hq in [0, w.Hq - 1] + [int(x) for x in rng.integers(0, w.Hq, 2)]:
-        rows = np.unique(np.concatenate([[0, w.Nq - 1], rng.integers(0, w.Nq, 24)]))
-        args = (exact[0][0, hq], exact[1][0, hq], exact[2][0, hq], w.scale, w.causal)
-        Ox, _ = oracle.attention_head(*args, rows=rows)
-        Op, Lp = oracle.fp8p_attention_head(*args, lean=lean, rows=rows)
+        rows = np.unique(np.concatenate([[0, w.Nq - 1], rng.integers(0, w.Nq, 16)]))
+        r, a = check_bounded(O[0, hq][rows].astype(np.float64), L[0, hq][rows].astype(np.float64), qc[0, hq],
+                             kc[0, hq], vv[0, hq], desc[0], desc[1], w.scale, w.causal, lean, rows)
+        worst, amb = max(worst, r), amb + [a]
+        Ox, _ = oracle.attention_head(qc[0, hq] * np.float64(desc[0]), kc[0, hq] * np.float64(desc[1]), vv[0, hq],
+                                      w.scale, w.causal, rows=rows)
         err_x.append(O[0, hq][rows] - Ox)
-        err_p.append(O[0, hq][rows] - Op)
         scale.append(Ox)
-        assert (np.abs(L[0, hq][rows] - Lp) / np.maximum(1.0, np.abs(Lp))).max() <= 1e-2
     rms = lambda a: float(np.sqrt((np.concatenate(a) ** 2).mean()))
-    note(f"  RMS vs exact {rms(err_x):.3e}, vs e4m3-P oracle {rms(err_p):.3e}, O scale {rms(scale):.3e}")
+    note(f"  worst |dO| / admissible {worst:.3f}; open decisions {np.mean(amb):.4f}; RMS vs exact "
+         f"{rms(err_x):.3e}, O scale {rms(scale):.3e}")
     assert rms(err_x) <= 2.0 ** -4 * rms(scale)
-    assert rms(err_p) <= 0.25 * rms(err_x)

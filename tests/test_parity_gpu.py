@@ -8,9 +8,11 @@ Element-by-element comparisons on seeded inputs from
   * the full-size workloads in the launch configuration the bench times,
     on sampled rows the oracle computes one by one.
 
-Tolerances: bf16 max |dO| <= 2e-2, fp8 <= 8e-2, fp32 <= 1e-4 (fp32 MFMA
-products, fp32 softmax; error is ~1e-6 in practice); LSE within
-1e-3 * max(1, |LSE|).
+Tolerances (``bars.py``): bf16 max |dO| <= 2e-2, fp8 <= 8e-2, fp32 <= 1e-4
+(fp32 MFMA products, fp32 softmax; error is ~1e-6 in practice); LSE within
+1e-3 * max(1, |LSE|); and the scale-aware bars that a dropped key tile fails
+at full size: every row within 2^-6 of its own largest |O_ref|, |dLSE| <=
+5e-4.  Repeat launches of every kernel configuration are bitwise equal.
 """
 import math
 import sys
@@ -20,13 +22,12 @@ import pytest
 import torch
 
 import oracle
+from bars import TOL_O, bar_violations, scales, scales_head
 from exact_io_aware_attn_amd import attn as A
 from exact_io_aware_attn_amd.inputs import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {"f32": 1e-4, "bf16": 2e-2, "fp8": 8e-2}
-TOL_LSE = 1e-3
 
 
 def note(msg):
@@ -39,6 +40,17 @@ def as64(t):
 
 def dequant(codes, d):
     return oracle.e4m3fn_decode(codes.view(torch.uint8).numpy()) * np.float64(d)
+
+
+def fp8_codes(w, inp):
+    """(q codes, k codes, dq, dk) of an e4m3 workload (the code values
+    without descales, whose dot products the fp8 matrix instruction forms),
+    or None."""
+    if w.dtype != "fp8":
+        return None
+    q8, k8, _, desc = inp
+    return (oracle.e4m3fn_decode(q8.view(torch.uint8).numpy()), oracle.e4m3fn_decode(k8.view(torch.uint8).numpy()),
+            desc[0], desc[1])
 
 
 def oracle_inputs(w, inp):
@@ -74,17 +86,10 @@ def run_gpu(w, inp, nan_fill=True, guard=0):
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
 
 
-def compare(w, O, L, Oref, Lref, tol_o=None):
-    tol_o = TOL_O[w.dtype] if tol_o is None else tol_o
-    assert np.isfinite(O).all(), "non-finite or unwritten output"
-    err = np.abs(O - Oref).max() if O.size else 0.0
-    assert err <= tol_o, f"max |dO| = {err:.3e} > {tol_o}"
-    fin = np.isfinite(Lref)
-    assert np.array_equal(np.isneginf(L), ~fin), "LSE -inf pattern differs"
-    if fin.any():
-        lerr = (np.abs(L[fin] - Lref[fin]) / np.maximum(1.0, np.abs(Lref[fin]))).max()
-        assert lerr <= TOL_LSE, f"LSE rel err {lerr:.3e}"
-    return err
+def compare(w, O, L, Oref, Lref, sc=None):
+    bad = bar_violations(O, L, Oref, Lref, w.dtype, sc=sc)
+    assert not bad, "; ".join(bad)
+    return float(np.abs(O - Oref).max()) if O.size else 0.0
 
 
 def full_parity(w, guard=64):
@@ -93,7 +98,7 @@ def full_parity(w, guard=64):
     O, L = run_gpu(w, inp, guard=guard)
     q, k, v = oracle_inputs(w, inp)
     Oref, Lref = oracle.attention(q, k, v, w.scale, w.causal)
-    return compare(w, O, L, Oref, Lref)
+    return compare(w, O, L, Oref, Lref, scales(q, k, v, w.scale, w.causal, Oref, Lref, fp8_codes(w, inp)))
 
 
 # ---------------------------------------------------------------------------
@@ -119,6 +124,13 @@ SMALL = [
     (1, 4, 2, 600, 1000, 128, True, "bf16"),
     (2, 2, 1, 777, 777, 64, True, "bf16"),
     (1, 2, 2, 513, 1500, 128, False, "bf16"),
+    # grids of 768 work-groups (three per compute unit: 32-key tiles at three
+    # waves per SIMD) over few keys, so each key tile carries a large share
+    # of every row: keyless causal rows, a ragged last tile, MHA and GQA
+    (1, 768, 768, 128, 77, 128, True, "bf16"),
+    (1, 768, 192, 100, 100, 128, True, "bf16"),
+    (1, 768, 192, 128, 77, 128, False, "bf16"),
+    (1, 768, 768, 100, 100, 128, False, "bf16"),
     # wide head dims: one or two key tiles only, keyless causal rows, tails
     (1, 2, 2, 64, 32, 320, False, "bf16"),
     (1, 2, 2, 129, 33, 256, False, "bf16"),
@@ -180,7 +192,8 @@ def test_splitd_scale_variants():
         torch.cuda.synchronize()
         qq, kk, vv = oracle_inputs(w, inp)
         Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
-        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref,
+                scales(qq, kk, vv, sc, True, Oref, Lref, fp8_codes(w, inp)))
 
 
 FP8_SMALL = [
@@ -221,7 +234,8 @@ def test_fp8_scale_variants():
         torch.cuda.synchronize()
         qq, kk, vv = oracle_inputs(w, inp)
         Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
-        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref,
+                scales(qq, kk, vv, sc, True, Oref, Lref, fp8_codes(w, inp)))
 
 
 def test_scale_variants_bf16():
@@ -234,7 +248,8 @@ def test_scale_variants_bf16():
         torch.cuda.synchronize()
         qq, kk, vv = oracle_inputs(w, inp)
         Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
-        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref,
+                scales(qq, kk, vv, sc, True, Oref, Lref, fp8_codes(w, inp)))
 
 
 def test_rows_sum_to_one_through_gpu():
@@ -294,8 +309,12 @@ def sampled_parity(w, n_heads=3, n_rows=48, seed=0):
     heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n_heads)]
     for b, hq in heads:
         rows = np.unique(np.concatenate([[0, 1, w.Nq - 1], rng.integers(0, w.Nq, n_rows)]))
-        Oref, Lref = oracle.attention_head(q[b, hq], k[b, hq // G], v[b, hq // G], w.scale, w.causal, rows=rows)
-        worst = max(worst, compare(w, O[b, hq][rows], L[b, hq][rows], Oref, Lref))
+        qh, kh, vh = q[b, hq], k[b, hq // G], v[b, hq // G]
+        Oref, Lref = oracle.attention_head(qh, kh, vh, w.scale, w.causal, rows=rows)
+        f8 = fp8_codes(w, inp)
+        f8 = None if f8 is None else (f8[0][b, hq], f8[1][b, hq // G], f8[2], f8[3])
+        sc = scales_head(qh, kh, vh, w.scale, w.causal, rows, Oref, Lref, f8)
+        worst = max(worst, compare(w, O[b, hq][rows], L[b, hq][rows], Oref, Lref, sc))
     assert np.isfinite(O).all() and not np.isnan(L).any()
     note(f"{w.name}: worst sampled max|dO| = {worst:.3e}")
 

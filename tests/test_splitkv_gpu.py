@@ -20,13 +20,12 @@ import pytest
 import torch
 
 import oracle
+from bars import bar_violations, scales, scales_head
 from exact_io_aware_attn_amd import attn as A
 from exact_io_aware_attn_amd.inputs import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {"f32": 1e-4, "bf16": 2e-2, "fp8": 8e-2}
-TOL_LSE = 1e-3
 
 
 def note(msg):
@@ -50,15 +49,11 @@ def gpu_and_oracle_inputs(w):
     return dev, descales, exact
 
 
-def check(O, L, Oref, Lref, tol_o):
-    assert np.isfinite(O).all(), "non-finite or unwritten output"
-    err = np.abs(O - Oref).max() if O.size else 0.0
-    assert err <= tol_o, f"max |dO| = {err:.3e} > {tol_o}"
-    fin = np.isfinite(Lref)
-    assert np.array_equal(np.isneginf(L), ~fin), "LSE -inf pattern differs"
-    if fin.any():
-        lerr = (np.abs(L[fin] - Lref[fin]) / np.maximum(1.0, np.abs(Lref[fin]))).max()
-        assert lerr <= TOL_LSE, f"LSE rel err {lerr:.3e}"
+def check(O, L, Oref, Lref, dtype, sc=None):
+    """The stated and the scale-aware bars (``bars.py``; the output bar
+    where the error scales ``sc`` are given)."""
+    bad = bar_violations(O, L, Oref, Lref, dtype, sc=sc)
+    assert not bad, "; ".join(bad)
 
 
 PARTIAL = [
@@ -88,7 +83,7 @@ def test_partial_parity(case):
     o, lse = A.fwd_partial(q, k, v, kb, ke, causal=causal, scale=w.scale, descales=desc)
     torch.cuda.synchronize()
     Oref, Lref = oracle.attention_range(qe, ke_, ve, w.scale, causal, kb, ke)
-    check(o.cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref, TOL_O[dt])
+    check(o.cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref, dt)
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -142,7 +137,13 @@ def test_splitkv_parity(case):
     o, lse = A.fwd_splitkv(q, k, v, ns, causal=causal, scale=w.scale, descales=desc)
     torch.cuda.synchronize()
     Oref, Lref = oracle.attention(qe, ke, ve, w.scale, causal)
-    check(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref, TOL_O[dt])
+    f8 = None
+    if dt == "fp8":
+        q8, k8, _, dsc = make_inputs(w)
+        f8 = (oracle.e4m3fn_decode(q8.view(torch.uint8).numpy()), oracle.e4m3fn_decode(k8.view(torch.uint8).numpy()),
+              dsc[0], dsc[1])
+    check(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref, dt,
+          scales(qe, ke, ve, w.scale, causal, Oref, Lref, f8))
 
 
 def test_splitkv_matches_plain_call():
@@ -183,6 +184,7 @@ def test_chunk_prefill_full_size_sampled(name):
     G = w.Hq // w.Hkv
     for b, hq in [(0, 0), (w.B - 1, w.Hq - 1), (0, int(rng.integers(w.Hq)))]:
         rows = np.unique(np.concatenate([[0, w.Nq - 1], rng.integers(0, w.Nq, 40)]))
-        Oref, Lref = oracle.attention_head(qh[b, hq].double().numpy(), kh[b, hq // G].double().numpy(),
-                                           vh[b, hq // G].double().numpy(), w.scale, w.causal, rows=rows)
-        check(O[b, hq][rows], L[b, hq][rows], Oref, Lref, TOL_O[w.dtype])
+        args = (qh[b, hq].double().numpy(), kh[b, hq // G].double().numpy(), vh[b, hq // G].double().numpy())
+        Oref, Lref = oracle.attention_head(*args, w.scale, w.causal, rows=rows)
+        check(O[b, hq][rows], L[b, hq][rows], Oref, Lref, w.dtype,
+              scales_head(*args, w.scale, w.causal, rows, Oref, Lref))
