@@ -20,7 +20,7 @@ ATTN_P_E4M3, ATTN_P_E4M3_LEAN = 1, 2
 
 # every symbol include/attn.h declares
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_partial", "attn_merge", "attn_splitkv_workspace_bytes",
-            "attn_fwd_splitkv", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_fp8_p", "attn_fwd_exp_poly",
+            "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_quantize_fp8", "attn_fwd_fp8_blocks", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_fp8_p", "attn_fwd_exp_poly",
             "attn_status_string",
             "attn_last_error", "attn_version")
 
@@ -59,6 +59,9 @@ def lib():
     L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, vp, vp, vp,
                                    i64, vp, ctypes.c_size_t, vp]
     L.attn_fwd_splitkv.restype = ci
+    L.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, ci, vp, vp, vp,
+                                           i64, vp]
+    L.attn_fwd_splitkv_noalloc.restype = ci
     L.attn_quantize_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp]
     L.attn_quantize_fp8.restype = ci
     L.attn_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, cf, vp, vp, vp, vp]
@@ -298,6 +301,27 @@ def fwd_splitkv(q, k, v, n_splits, causal=False, scale=None, descales=None, work
                                   _stream_ptr(stream)))
     return o, lse
 
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def fwd_splitkv_noalloc(q, k, v, n_splits, causal=False, scale=None, descales=None, out=None, lse=None,
+                        stream=None):
+    """``fwd_splitkv`` through ``attn_fwd_splitkv_noalloc``: the partial
+    results live in the library's fixed per-GPU scratch area, so the C call
+    allocates nothing (``out`` and ``lse`` are allocated here unless given).
+    Calls that overlap on one GPU race on that area."""
+    B, Hq, Hkv, Nq, Nkv, D = _shapes(q, k, v)
+    dt = _dtype_code(q, k, v)
+    dptr = _descale_ptrs(dt, descales)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = _buffer(out, "out", (B, Hq, Nq, D), torch.float32 if dt == ATTN_F32 else torch.bfloat16, q.device)
+    lse = _buffer(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
+    _check(lib().attn_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                          B, Hq, Hkv, Nq, Nkv, D, int(causal), float(scale), dt, *dptr,
+                                          int(n_splits), _stream_ptr(stream)))
+    return o, lse
 
 def quantize_fp8(x, signs=None, codes=None, descales=None, stream=None):
     """Block e4m3 quantisation of a bf16 (B, H, N, D) device tensor, one

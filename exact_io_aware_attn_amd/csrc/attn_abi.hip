@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "attn.h"
 #include "attn_common.h"
@@ -202,6 +203,38 @@ int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse
   mp.lse_part_stride = l_bytes / 4;
   hipError_t err = attn::launch_merge(mp, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch failed: %s", hipGetErrorString(err));
+  return ATTN_OK;
+}
+
+// Scratch of attn_fwd_splitkv_noalloc: device memory of fixed size at file
+// scope, so the entry point allocates nothing.  Each GPU the library runs on
+// holds its own copy, from the loading of this code object until the
+// process ends; calls on one GPU share it (the last call's partial results
+// stay in it).  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address is taken once per device, with that
+// device current, by hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || ptr == nullptr)
+      return fail(ATTN_ERR_HIP, "hipGetSymbolAddress of the scratch area failed: %s", hipGetErrorString(err));
+    if (reinterpret_cast<uintptr_t>(ptr) & 255u)
+      return fail(ATTN_ERR_HIP, "the scratch area is not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return ATTN_OK;
 }
 
@@ -411,6 +444,27 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   return splitkv_run(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q, descale_k, descale_v,
                      n_splits, workspace, stream);
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                             int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, int causal, float scale,
+                             int dtype, const float* descale_q, const float* descale_k, const float* descale_v,
+                             int64_t n_splits, attn_stream_t stream) {
+  g_last_error[0] = '\0';
+  const int st = splitkv_check(q, k, v, o, B, Hq, Hkv, Nq, Nkv, D, scale, dtype, descale_q, descale_k, descale_v,
+                               n_splits);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_splitkv_workspace_bytes(B, Hq, Nq, D, n_splits);
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "the partial results need %zu bytes, more than the %zu-byte scratch of attn_fwd_splitkv_noalloc "
+                "(use attn_fwd_splitkv with a caller workspace, or fewer splits)",
+                need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int sst = scratch_address(&ws);
+  if (sst != ATTN_OK) return sst;
+  return splitkv_run(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype, descale_q, descale_k, descale_v,
+                     n_splits, ws, stream);
 }
 
 const char* attn_status_string(int status) {

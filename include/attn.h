@@ -234,6 +234,37 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      const float* descale_q, const float* descale_k, const float* descale_v,
                      int64_t n_splits, void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* Size of the scratch area of attn_fwd_splitkv_noalloc, per GPU: 64 MiB. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same two launches on `stream`, with the
+ * partial results in a scratch area the library holds at file scope
+ * (ATTN_NOALLOC_SCRATCH_BYTES of device memory on each GPU it runs on, from
+ * the loading of the library's code until the process ends) instead of a
+ * caller workspace.  The call allocates nothing: no hipMalloc, no library
+ * allocator.
+ *   Arguments, outputs and results as attn_fwd_splitkv without workspace
+ *   and workspace_bytes.
+ *   ATTN_ERR_UNSUPPORTED when attn_splitkv_workspace_bytes(B, Hq, Nq, D,
+ *   n_splits) exceeds ATTN_NOALLOC_SCRATCH_BYTES (use attn_fwd_splitkv, or
+ *   fewer splits).
+ * All calls on one GPU share its scratch area, which keeps the last call's
+ * partial results (nothing in it needs clearing: each call writes every
+ * partial element before reading it).  Calls that overlap on one GPU --
+ * concurrent streams, or host threads enqueueing on different streams --
+ * race on it and must be serialised by the caller.  The first call on each
+ * GPU resolves the scratch area's device address (hipGetSymbolAddress):
+ * make it once before any graph capture that records this call.
+ */
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                             int causal, float scale, int dtype,
+                             const float* descale_q, const float* descale_k, const float* descale_v,
+                             int64_t n_splits, attn_stream_t stream);
+
 /*
  * The fp8 input pipeline (FA blog, section "FA3 — el momento Hopper": FP8
  * with one scale per 64 x d tile and a random orthogonal Hadamard-based

@@ -255,3 +255,32 @@ def test_binding_output_buffer_checks():
         A._workspace(ws, 101, dev)
     assert A._workspace(torch.empty(30, dtype=torch.float32), 120, dev).numel() == 30
 
+
+def noalloc(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, D=128, causal=0,
+            scale=0.1, dtype=A.ATTN_BF16, n_splits=2):
+    return A.lib().attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, causal, scale, dtype,
+                                            None, None, None, n_splits, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(o=None), dict(q=FAKE + 8), dict(B=0), dict(Hq=3, Hkv=2), dict(Hkv=0),
+    dict(scale=float("nan")), dict(dtype=9), dict(n_splits=0), dict(n_splits=5000),
+])
+def test_noalloc_invalid_arguments(kw):
+    assert noalloc(**kw) == A.ATTN_ERR_INVALID_ARG
+    assert A.lib().attn_last_error() != b""
+
+
+def test_noalloc_scratch_limit():
+    # 32 heads x 4096 rows x 128 x 4 bytes x 8 splits = 512 MiB of partials
+    assert A.splitkv_workspace_bytes(1, 32, 4096, 128, 8) > A.NOALLOC_SCRATCH_BYTES
+    assert noalloc(Hq=32, Hkv=8, Nq=4096, Nkv=4096, n_splits=8) == A.ATTN_ERR_UNSUPPORTED
+    assert b"scratch" in A.lib().attn_last_error()
+    hdr = open(HEADER).read()
+    assert re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
+    assert A.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="a GPU is visible: the call would launch")
+def test_noalloc_without_device_returns_hip_error():
+    assert noalloc() == A.ATTN_ERR_HIP
