@@ -72,11 +72,14 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_io_aware_
 # sources of the direct-to-LDS and e4m3-probability kernels (the launch
 # rules, causal tile pairing included, live in attn_launch.h)
 _PIPE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_pipe.hip")
+# sources of the bf16 kernel of head dims 64 and 128
+_BF16 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_bf16.hip")
 _P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (_PIPE, "e207c00edc922816", 271829.46875 * 2 * 1024, 133294.953125 * 1024),
-    "gqa_causal_bf16": (_PIPE, "e207c00edc922816", 196709.40625 * 2 * 1024, 133120.171875 * 1024),
+    "prefill_causal_bf16": (_BF16, "3eca75bc6e411aea", 277459.21875 * 2 * 1024, 137317.703125 * 1024),
+    "gqa_causal_bf16": (_BF16, "3eca75bc6e411aea", 199771.0625 * 2 * 1024, 137221.09375 * 1024),
+    "gqa_cross_bf16": (_BF16, "3eca75bc6e411aea", 67881.5625 * 2 * 1024, 35328.0 * 1024),
     "fp8_outlier": (_PIPE, "e207c00edc922816", 189905.09375 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
@@ -87,7 +90,7 @@ MEASURED_TRAFFIC = {
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
-    "chunk_prefill_splitkv_bf16": (_PIPE, "e207c00edc922816", 73783.5 * 2 * 1024, 33024.0 * 1024),
+    "chunk_prefill_splitkv_bf16": (_BF16, "3eca75bc6e411aea", 73817.5625 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
     "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.hip"), "62725cf06fe17335",
                         667898.9375 * 2 * 1024, 397492.28125 * 1024),

@@ -1,6 +1,8 @@
 // attn_fwd_pipe.hip -- attention forward for gfx950 with direct-to-LDS K/V
-// streaming: bf16 for head dims 64 and 128 and e4m3 (fp8) for 64, 128 and
-// 256, positive scale.  (bf16 at larger head dims runs the wide-head kernel.)
+// streaming: e4m3 (fp8) for head dims 64, 128 and 256, and the bf16 variant
+// with a polynomial exponential (D = 64, 128), positive scale.  (Plain bf16
+// runs attn_fwd_bf16.hip at D = 64 and 128 and the wide-head kernel at
+// larger head dims.)
 //
 // Same algorithm as the generic tiled kernel (FlashAttention summary page,
 // method paragraph; blog post "FlashAttention v1/v2/v3/v4", section "El truco
@@ -583,21 +585,6 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// bf16 D = 128: 32-key tiles at three waves per SIMD (165 VGPRs; 32 KiB of
-// LDS per work-group) where the grid gives every CU at least three
-// work-groups, otherwise 64-key tiles at two.  Same-box A/B against 64-key
-// tiles: causal prefill +2.8 %, GQA causal +1.6 %, GQA cross +0.2 %; a
-// 512-work-group split-KV chunk, which cannot fill the third slot, -2.3 %.
-hipError_t launch_pipe_bf16_d128(const FwdParams& p0, hipStream_t stream) {
-  using C = PipeCfg<ELT_BF16, 128, 4, 2, 32>;
-  FwdParams p = p0;
-  p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  p.pair_causal = pair_causal_tiles(p);
-  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);
-  return total >= 3 * (int64_t)cu_count() ? launch_pipe<ELT_BF16, 128, 4, 2, 32>(p0, stream)
-                                            : launch_pipe<ELT_BF16, 128, 4, 2, 64>(p0, stream);
-}
-
 }  // namespace
 
 LaunchFn pipe_launcher(int elt, int D) {
@@ -611,12 +598,7 @@ LaunchFn pipe_launcher(int elt, int D) {
     }
   }
   if (elt != ELT_BF16) return nullptr;
-  switch (D) {
-    // two work-groups of 4 waves per CU, 64-key tiles, double-buffered
-    case 64: return &launch_pipe<ELT_BF16, 64, 4, 2, 64>;
-    case 128: return &launch_pipe_bf16_d128;
-    default: return nullptr;
-  }
+  return bf16_launcher(D);  // attn_fwd_bf16.hip
 }
 
 LaunchFn pipe_poly_launcher(int D) {

@@ -108,9 +108,13 @@ __host__ __device__ inline int qtile_slots(const FwdParams& p) {
 // (attn::Elt) and head dim D, or nullptr if that pair is not instantiated.
 LaunchFn tiled_launcher(int elt, int D);
 
-// Launcher for the direct-to-LDS kernel (bf16: D = 64 or 128; e4m3: D = 64,
-// 128 or 256; scale > 0), or nullptr.
+// Launcher for the direct-to-LDS kernel (bf16: D = 64 or 128, through
+// bf16_launcher; e4m3: D = 64, 128 or 256; scale > 0), or nullptr.
 LaunchFn pipe_launcher(int elt, int D);
+
+// Launcher for the bf16 kernel of head dims 64 and 128 (scale > 0), or
+// nullptr.
+LaunchFn bf16_launcher(int D);
 
 // Launcher for the software-pipelined wide-head kernel (bf16, D a multiple
 // of 64 in [192, 512], scale > 0), or nullptr.

@@ -4,7 +4,7 @@ cross-compiles without a GPU).
 Each kernel source is compiled to assembly with the library's own flags and
 every kernel in it is checked for properties the design relies on:
 
-* no scratch (register spills), apart from two known, bounded cases (stored
+* no scratch (register spills), apart from a few known, bounded cases (stored
   before the key loop and reloaded in the epilogue);
 * no packed fp32 instructions (the build disables them);
 * M0 written only inside the inline assembly of the direct-to-LDS loads, so
@@ -23,12 +23,15 @@ import pytest
 
 from exact_io_aware_attn_amd import build as B
 
-KERNEL_SOURCES = ("attn_fwd_pipe.hip", "attn_fwd_wide.hip", "attn_fwd_splitd.hip", "attn_fwd_tiled.hip",
+KERNEL_SOURCES = ("attn_fwd_bf16.hip", "attn_fwd_pipe.hip", "attn_fwd_wide.hip", "attn_fwd_splitd.hip", "attn_fwd_tiled.hip",
                   "attn_merge.hip", "attn_quant.hip", "attn_bwd.hip", "attn_fwd_p8.hip")
 
 # kernels allowed a small spill: (source, kernel name fragment) -> max bytes
 # (Q takes D/8 or D/4 VGPRs and O every accumulation register at these D)
 KNOWN_SCRATCH = {
+    # one 64-bit value kept across the key loop at three waves per SIMD
+    # (168 of 170 VGPRs): stored before the loop, reloaded after it
+    ("attn_fwd_bf16.hip", "attn_fwd_bf16_kernelILi128ELi32E"): 12,
     ("attn_fwd_wide.hip", "attn_fwd_wide_kernelILi512E"): 24,
     ("attn_fwd_splitd.hip", "attn_fwd_splitd_kernelILi1024E"): 8,
 }
