@@ -70,12 +70,13 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   if (B * Hq * ((Nq + 31) / 32) * n_splits >= lim)
     return fail(ATTN_ERR_UNSUPPORTED, "grid too large: splits*B*Hq*ceil(Nq/32) must be < 2^31");
 
+  // bf16 D = 1024 runs on the eight-wave split-D kernel (any scale).
   // The wide-head kernel (bf16, D a multiple of 64 in [192, 512]) and the
   // direct-to-LDS kernel (bf16, D = 64 or 128; e4m3, D = 64, 128 or 256) fold
   // the scale into one FMA before exp2 and take row maxima of the unscaled
   // scores, which needs scale > 0.  Every other D <= 256 case runs on the
-  // generic tiled kernel and every other D > 256 case on the split-D kernels;
-  // both scale before masking.
+  // generic tiled kernel and every other D > 256 case on the four-wave
+  // split-D kernel; both scale before masking.
   attn::LaunchFn fn = nullptr;
   if (p_mode != 0) {
     // e4m3 probabilities: the fp8 P V kernel only
@@ -99,6 +100,7 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
       return fail(ATTN_ERR_UNSUPPORTED, "block-scaled e4m3 needs D in {64, 128, 256} and scale > 0 (D=%lld)",
                   (long long)D);
   }
+  if (!fn) fn = attn::splitd8_launcher(elt, (int)D);
   if (!fn && scale > 0.0f) fn = attn::wide_launcher(elt, (int)D);
   if (!fn && scale > 0.0f) fn = attn::pipe_launcher(elt, (int)D);
   if (!fn) fn = D <= 256 ? attn::tiled_launcher(elt, (int)D) : attn::splitd_launcher(elt, (int)D);

@@ -1,5 +1,6 @@
 // attn_fwd_splitd.hip -- exact attention forward for large head dims
-// (bf16, D a multiple of 64 in [320, 1024]) on gfx950.
+// (bf16, D a multiple of 64 in [320, 960]; D = 1024 has its own eight-wave
+// kernel, attn_fwd_splitd8.hip) on gfx950.
 //
 // FFPA README, section "Split-D and TiledMMA": two things grow with D -- the
 // on-chip footprint of the Q/K/V tiles and the registers of the output
@@ -10,7 +11,7 @@
 //  * A work-group has 4 waves = 2 query halves (32 rows each) x 2 head-dim
 //    halves (D/2 columns each).  Wave (qh, dh) keeps Q[32 rows, D/2 cols] in
 //    registers and accumulates O^T[D/2 rows, 32 queries] -- D/8 + D/4
-//    registers per lane, so D = 1024 fits (128 VGPRs of Q, 256 accumulator
+//    registers per lane, so D = 960 fits (120 VGPRs of Q, 240 accumulator
 //    registers) where a wave owning all of D would need twice that.  The two
 //    halves are interleaved: for S, wave dh owns the 16-column chunks
 //    2cc + dh; for O, the 32-column blocks 2db + dh.  With the XOR swizzle
@@ -25,7 +26,7 @@
 //    multiplies P by its own D/2 columns of V.
 //  * K and V tiles of 32 keys stream into LDS with direct-to-LDS buffer
 //    loads (zero past Nkv) using the same XOR swizzles as the D <= 128
-//    kernel.  At D = 1024 one K tile and one V tile already take 128 KiB of
+//    kernel.  At D = 960 one K tile and one V tile already take 120 KiB of
 //    the 160 KiB LDS, so each is single-buffered and the two loads are
 //    staggered: K(t+1) streams in while the softmax and P V of tile t run, and
 //    V(t+1) streams in while the scores of tile t+1 are computed.  Two
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   dma_offsets<C, false>(dk, wave, lane);
   dma_offsets<C, true>(dv, wave, lane);
   // offset of load block j inside the loop: recomputed when the row pitch
-  // allows it (D = 512, 1024), which frees the 2 DMA_WAVE offset registers
+  // allows it (D = 512), which frees the 2 DMA_WAVE offset registers
   auto dma_off = [&](bool is_v, int j) -> uint32_t {
     if constexpr (C::RP % 1024 == 0)
       return is_v ? dma_offset_1k<C, true>(wave, lane, j) : dma_offset_1k<C, false>(wave, lane, j);
@@ -357,7 +358,6 @@ LaunchFn splitd_launcher(int elt, int D) {
     case 832: return &launch_splitd<832>;
     case 896: return &launch_splitd<896>;
     case 960: return &launch_splitd<960>;
-    case 1024: return &launch_splitd<1024>;
     default: return nullptr;
   }
 }

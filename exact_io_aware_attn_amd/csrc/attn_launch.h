@@ -120,8 +120,13 @@ LaunchFn bf16_launcher(int D);
 // of 64 in [192, 512], scale > 0), or nullptr.
 LaunchFn wide_launcher(int elt, int D);
 
-// Launcher for the split-D kernels (bf16, 256 < D <= 1024), or nullptr.
+// Launcher for the four-wave split-D kernel (bf16, D a multiple of 64 in
+// [320, 960]), or nullptr.
 LaunchFn splitd_launcher(int elt, int D);
+
+// Launcher for the eight-wave split-D kernel (bf16, D = 1024; any scale), or
+// nullptr.
+LaunchFn splitd8_launcher(int elt, int D);
 
 // Log-sum-exp merge of partial results: part i of o_parts (rows, D) starts
 // at o_parts + i * o_part_stride and part i of lse_parts (rows) at

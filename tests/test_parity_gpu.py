@@ -173,6 +173,14 @@ SPLITD_SMALL = [
     (1, 2, 2, 70, 200, 1024, False),
     (1, 2, 2, 129, 129, 1024, True),
     (1, 1, 1, 1, 1, 640, False),
+    # eight-wave kernel (D = 768, 1024): one key tile, a one-key tail tile,
+    # more queries than keys (causal rows and whole query halves that see no
+    # key), several query tiles on the diagonal, a single element
+    (1, 2, 2, 64, 32, 1024, False),
+    (1, 2, 1, 100, 33, 768, False),
+    (1, 3, 1, 200, 64, 1024, True),
+    (2, 2, 2, 300, 300, 768, True),
+    (1, 1, 1, 1, 1, 1024, False),
 ]
 
 
@@ -183,9 +191,10 @@ def test_splitd_small_parity(case):
     full_parity(Workload("splitd", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", value_scale=0.5, seed=D + Nq))
 
 
-def test_splitd_scale_variants():
+@pytest.mark.parametrize("D", [512, 1024])
+def test_splitd_scale_variants(D):
     for sc in (0.0, -0.05):
-        w = Workload("sdscale", 1, 2, 1, 80, 100, 512, True, "bf16", value_scale=0.5, seed=4)
+        w = Workload("sdscale", 1, 2, 1, 80, 100, D, True, "bf16", value_scale=0.5, seed=4)
         inp = make_inputs(w)
         q, k, v = (t.cuda() for t in inp)
         o, lse = A.fwd(q, k, v, causal=True, scale=sc)
@@ -194,6 +203,39 @@ def test_splitd_scale_variants():
         Oref, Lref = oracle.attention(qq, kk, vv, sc, True)
         compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref,
                 scales(qq, kk, vv, sc, True, Oref, Lref, fp8_codes(w, inp)))
+
+
+GROWING = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal)
+    (1, 2, 1, 150, 300, 1024, False),
+    (1, 2, 2, 200, 200, 768, True),
+    (1, 2, 1, 100, 260, 512, False),
+    (1, 2, 2, 300, 333, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", GROWING, ids=lambda c: "Nq{}_Nkv{}_D{}_{}".format(
+    *c[3:6], "causal" if c[6] else "full"))
+def test_growing_scores_parity(case):
+    """Scores that grow along the key axis by a quarter per key (11.5 in
+    exp2 units per 32 keys): each key tile raises the running maximum far past
+    the lazy-rescale thresholds, so the rescale path runs on (almost) every
+    tile, and each row's weight sits on its last few visible keys."""
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    w = Workload("growing", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", value_scale=0.5, seed=D + Nkv)
+    note(f"growing B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal}")
+    q, k, v = make_inputs(w)
+    # channel 0: 4 in every query, a * j in key j, so q.k gains 4 a / sqrt(D) = 1/4 per key
+    a = math.sqrt(D) / 16.0
+    q = q.float()
+    k = k.float()
+    q[..., 0] = 4.0
+    k[..., 0] = a * torch.arange(Nkv, dtype=torch.float32)
+    inp = (q.to(torch.bfloat16), k.to(torch.bfloat16), v)
+    O, L = run_gpu(w, inp, guard=64)
+    qq, kk, vv = oracle_inputs(w, inp)
+    Oref, Lref = oracle.attention(qq, kk, vv, w.scale, causal)
+    compare(w, O, L, Oref, Lref, scales(qq, kk, vv, w.scale, causal, Oref, Lref, None))
 
 
 FP8_SMALL = [
