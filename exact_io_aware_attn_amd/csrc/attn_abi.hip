@@ -106,7 +106,7 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   if (!fn) fn = D <= 256 ? attn::tiled_launcher(elt, (int)D) : attn::splitd_launcher(elt, (int)D);
   if (!fn)
     return fail(ATTN_ERR_UNSUPPORTED, "no kernel for dtype=%d D=%lld (fp32: D%%32==0, D<=128; fp8: D%%64==0, "
-                "D<=256; bf16: D%%32==0, D<=256, or D%%64==0 in [320, 1024])", dtype, (long long)D);
+                "D<=256; bf16: D%%32==0, D<=1024)", dtype, (long long)D);
 
   attn::FwdParams p{};
   p.q = q;
@@ -119,6 +119,7 @@ int run_forward(const void* q, const void* k, const void* v, void* o, float* lse
   p.Hkv = (int)Hkv;
   p.Nq = (int)Nq;
   p.Nkv = (int)Nkv;
+  p.D = (int)D;
   p.group = (int)(Hq / Hkv);
   p.causal = causal ? 1 : 0;
   p.kv_off = (int)(Nkv - Nq);

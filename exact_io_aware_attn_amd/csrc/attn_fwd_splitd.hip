@@ -1,5 +1,5 @@
 // attn_fwd_splitd.hip -- exact attention forward for large head dims
-// (bf16, D a multiple of 64 in [320, 960]; D = 1024 has its own eight-wave
+// (bf16, D a multiple of 32 in [288, 992]; D = 1024 has its own eight-wave
 // kernel, attn_fwd_splitd8.hip) on gfx950.
 //
 // FFPA README, section "Split-D and TiledMMA": two things grow with D -- the
@@ -34,6 +34,12 @@
 //  * Causal masking, tails, lazy rescale (tau = 8, exact), XCD-contiguous
 //    work-group ranges and heaviest-first causal order as in the other
 //    kernels.
+//  * A head dim that is an odd multiple of 32 runs at the layout of the next
+//    multiple of 64, DP = D + 32: the 32 extra columns of each K/V row in LDS
+//    hold whatever the loads bring (the start of the next row, or zeros past
+//    the slab), the matching Q columns are zero, so the scores are exact,
+//    and the extra 32 output columns are not stored.  HBM addressing uses the
+//    real row pitch 2D throughout.
 #include "attn_common.h"
 #include "attn_dma.h"
 #include "attn_launch.h"
@@ -76,9 +82,12 @@ struct SplitCfg {
   static_assert(NQC == 2 * DMA_WAVE && 2 * NDB == 2 * DMA_WAVE, "load interleave");
 };
 
-template <int D>
+// DP: the layout's head dim (a multiple of 64); the real one is p.D, DP or
+// DP - 32.
+template <int DP>
 __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
-  using C = SplitCfg<D>;
+  using C = SplitCfg<DP>;
+  const int D = p.D;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   char* const kbuf = lds;
   char* const vbuf = lds + C::TILE;
@@ -121,16 +130,38 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   if (p.causal) kv_end = min(kr.nkv, min(q0 + C::BR, p.Nq) + kr.kv_off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
+  // Per-lane HBM offsets of this wave's direct-to-LDS loads: block j covers
+  // LDS tile bytes [(wave DMA_WAVE + j) KiB, +1 KiB) of RP-byte rows; lane l
+  // writes 16 of them and fetches the 16-byte chunk the swizzle places there,
+  // from the HBM row of pitch 2D.
+  const uint32_t gpitch = (uint32_t)(2 * D);
+  const uint32_t gtile = (uint32_t)C::BC * gpitch;  // one key tile in HBM
+  auto dma_at = [&](bool is_v, int j) -> uint32_t {
+    const int o = (wave * C::DMA_WAVE + j) * 1024 + lane * 16;
+    const int row = o / C::RP;
+    const int pc = (o - row * C::RP) >> 4;
+    const int gc = pc ^ (is_v ? v_swz<DP>(row) : k_swz<DP>(row));
+    return (uint32_t)row * gpitch + (uint32_t)(gc << 4);
+  };
   uint32_t dk[C::DMA_WAVE], dv[C::DMA_WAVE];
-  dma_offsets<C, false>(dk, wave, lane);
-  dma_offsets<C, true>(dv, wave, lane);
+#pragma unroll
+  for (int j = 0; j < C::DMA_WAVE; ++j) {
+    dk[j] = dma_at(false, j);
+    dv[j] = dma_at(true, j);
+  }
   // offset of load block j inside the loop: recomputed when the row pitch
-  // allows it (D = 512), which frees the 2 DMA_WAVE offset registers
+  // makes a block one LDS row (DP = 512, 1024: the row, and so its swizzle
+  // key, is uniform), which frees the 2 DMA_WAVE offset registers
   auto dma_off = [&](bool is_v, int j) -> uint32_t {
-    if constexpr (C::RP % 1024 == 0)
-      return is_v ? dma_offset_1k<C, true>(wave, lane, j) : dma_offset_1k<C, false>(wave, lane, j);
-    else
+    if constexpr (C::RP % 1024 == 0) {
+      constexpr int BPR = C::RP / 1024;  // blocks per row
+      const int blk = wave * C::DMA_WAVE + j;
+      const int row = blk / BPR;
+      const int gc = ((blk % BPR) * 64 + lane) ^ (is_v ? v_swz<DP>(row) : k_swz<DP>(row));
+      return (uint32_t)row * gpitch + (uint32_t)(gc << 4);
+    } else {
       return is_v ? dv[j] : dk[j];
+    }
   };
   if (n_kt > 0) {
     dma_tile<C>(rk, lk, dk, wave);
@@ -141,7 +172,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   {
     const uint32_t row_off = (uint32_t)qrow * (uint32_t)(D * 2) + (uint32_t)(dh * 32 + h * 16);
 #pragma unroll
-    for (int cc = 0; cc < C::NQC; ++cc) qf[cc] = buf_load16(rq, row_off + (uint32_t)(cc * 64));
+    for (int cc = 0; cc < C::NQC; ++cc)
+      qf[cc] = 32 * cc < D ? buf_load16(rq, row_off + (uint32_t)(cc * 64)) : u32x4{};  // zero past D
   }
 
   f32x16 acc[C::NDB];
@@ -153,8 +185,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   // K fragment: row l32, 16-byte chunk 4 cc + 2 dh + h.  The swizzle XORs
   // the low KB bits (KB = 3 or 4), so with G = 2^KB / 4 the address is
   // kbase[cc % G] + (cc / G) * 2^KB * 16.
-  constexpr int KG = (D % 128 == 0) ? 4 : 2;
-  const int kx = k_swz<D>(l32);
+  constexpr int KG = (DP % 128 == 0) ? 4 : 2;
+  const int kx = k_swz<DP>(l32);
   uint32_t kbase[KG];
 #pragma unroll
   for (int i = 0; i < KG; ++i) kbase[i] = (uint32_t)(l32 * C::RP + (((4 * i + 2 * dh + h) ^ kx) << 4));
@@ -163,14 +195,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   // 8 db + vlow with vlow = 4 dh + 2 (g16 & 1) + (r16 & 3) / 2; with
   // VG = 2^VB / 8 (VB = swizzle width in bits) the address is
   // vbase[db % VG] + (db / VG) * 2^VB * 16.
-  constexpr int VG = (D % 128 == 0) ? 2 : 1;
+  constexpr int VG = (DP % 128 == 0) ? 2 : 1;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int vrow0 = 4 * h + (r16 >> 2);
   const int vlow = 4 * dh + 2 * (g16 & 1) + ((r16 & 3) >> 1);
   uint32_t vbase[VG];
 #pragma unroll
   for (int i = 0; i < VG; ++i)
-    vbase[i] = (uint32_t)(vrow0 * C::RP + (((8 * i + vlow) ^ v_swz<D>(vrow0)) << 4) + ((r16 & 1) << 3));
+    vbase[i] = (uint32_t)(vrow0 * C::RP + (((8 * i + vlow) ^ v_swz<DP>(vrow0)) << 4) + ((r16 & 1) << 3));
   // partial-S exchange slots: wave w writes [w][j][lane] (16 B per lane, j = 0..3)
   char* const xmine = xch + wave * 4096 + lane * 16;
   const char* const xpeer = xch + (wave ^ 1) * 4096 + lane * 16;
@@ -186,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     // (even and odd chunks, where registers allow) so that consecutive MFMAs
     // do not depend on each other.  V(kt) streams into its (free) buffer meanwhile, one block per
     // two MFMAs (the first tile's V came with the prologue).
-    const i32x4 rv_t = rsrc_at(rv, (uint32_t)(kt * C::TILE));
+    const i32x4 rv_t = rsrc_at(rv, (uint32_t)kt * gtile);
     f32x16 s;
     {
       auto kaddr = [&](int cc) { return kbase[cc % KG] + (uint32_t)((cc / KG) * KG * 64); };
@@ -219,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     // K(kt+1): the first KS blocks now (their issue overlaps the exchange
     // read and the softmax), the rest between the PV MFMAs below
     const bool k_next = kt + 1 < n_kt;
-    const i32x4 rk_n = rsrc_at(rk, (uint32_t)((kt + 1) * C::TILE));
+    const i32x4 rk_n = rsrc_at(rk, (uint32_t)(kt + 1) * gtile);
     if (k_next) {
 #pragma unroll
       for (int j = 0; j < C::KS; ++j) dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, j), wave, j);
@@ -317,6 +349,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
     const int64_t orow = split * p.o_split_stride + q_slab + (int64_t)qrow * D + dh * 32;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
+      if (db * 64 + dh * 32 >= D) continue;  // padding columns
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 64 + 8 * g + 4 * h;
@@ -330,23 +363,25 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
   }
 }
 
-template <int D>
+template <int DP>
 hipError_t launch_splitd(const FwdParams& p0, hipStream_t stream) {
-  using C = SplitCfg<D>;
+  using C = SplitCfg<DP>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * p.n_qtiles;
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_splitd_kernel<D>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_splitd_kernel<DP>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// D a multiple of 32 in [288, 992]; an odd multiple of 32 runs at the
+// layout of D + 32.
 LaunchFn splitd_launcher(int elt, int D) {
-  if (elt != ELT_BF16) return nullptr;
-  switch (D) {
+  if (elt != ELT_BF16 || D % 32 != 0 || D < 288 || D > 992) return nullptr;
+  switch (D % 64 == 0 ? D : D + 32) {
     case 320: return &launch_splitd<320>;
     case 384: return &launch_splitd<384>;
     case 448: return &launch_splitd<448>;
@@ -358,6 +393,7 @@ LaunchFn splitd_launcher(int elt, int D) {
     case 832: return &launch_splitd<832>;
     case 896: return &launch_splitd<896>;
     case 960: return &launch_splitd<960>;
+    case 1024: return &launch_splitd<1024>;
     default: return nullptr;
   }
 }

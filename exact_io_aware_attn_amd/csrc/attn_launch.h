@@ -19,6 +19,7 @@ struct FwdParams {
   void* o;
   float* lse;          // may be null
   int B, Hq, Hkv, Nq, Nkv;
+  int D;               // head dim (a kernel may run at a padded size of its own)
   int group;           // Hq / Hkv
   int causal;          // 0 or 1
   int kv_off;          // Nkv - Nq: key j visible to query i iff j <= i + kv_off

@@ -35,9 +35,9 @@
  *  production-grade" (determinism; LSE lets key-range results merge).
  *
  *  Supported sizes: B, Hq, Hkv, Nq, Nkv >= 1.  Head dim D: ATTN_BF16 any
- *    multiple of 32 in [32, 256] or any multiple of 64 in [320, 1024] (the
- *    split-D kernels); ATTN_F32 a multiple of 32 in [32, 128]; fp8 a multiple
- *    of 64 in [64, 256].  Each (batch, head) slab of q, k, v and o must be
+ *    multiple of 32 in [32, 1024] (above 256 on the split-D kernels, an odd
+ *    multiple of 32 at the layout of D + 32); ATTN_F32 a multiple of 32 in
+ *    [32, 128]; fp8 a multiple of 64 in [64, 256].  Each (batch, head) slab of q, k, v and o must be
  *    smaller than 2^31 bytes; B*Hq*ceil(Nq/32) < 2^31.
  *
  * Ownership, synchronisation and errors

@@ -2,7 +2,8 @@
 
 The library must load, export every function ``include/attn.h`` declares,
 and reject invalid arguments with the documented codes before anything is
-enqueued (validation returns before any HIP call).
+enqueued (validation returns before any HIP call).  On a machine with no GPU
+a fully valid call returns ATTN_ERR_HIP (skipped where a GPU is visible).
 """
 import ctypes
 import os
@@ -65,7 +66,7 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(D=48), dict(D=1056), dict(D=2048), dict(D=288), dict(D=352),
+    dict(D=48), dict(D=1056), dict(D=2048), dict(D=1000),
     dict(D=256, dtype=A.ATTN_F32), dict(D=96, dtype=A.ATTN_FP8_E4M3), dict(D=512, dtype=A.ATTN_FP8_E4M3),
     dict(D=512, dtype=A.ATTN_F32),
     dict(Nkv=(1 << 31) // 256, D=128),            # K slab reaches 2^31 bytes
@@ -73,6 +74,15 @@ def test_invalid_arguments(kw):
 ])
 def test_unsupported(kw):
     assert call(**kw) == A.ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is visible: this call on fake pointers would launch")
+@pytest.mark.parametrize("D", [128, 288, 1024])
+def test_valid_call_without_a_device_reports_hip_error(D):
+    # every argument valid, no GPU in the machine: the launch fails in the
+    # HIP runtime, which the ABI reports as ATTN_ERR_HIP with its message
+    assert call(D=D) == A.ATTN_ERR_HIP
+    assert b"device" in A.lib().attn_last_error()
 
 
 def test_fp8_descale_alignment():

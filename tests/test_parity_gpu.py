@@ -181,6 +181,13 @@ SPLITD_SMALL = [
     (1, 3, 1, 200, 64, 1024, True),
     (2, 2, 2, 300, 300, 768, True),
     (1, 1, 1, 1, 1, 1024, False),
+    # odd multiples of 32: the four-wave kernel at the layout of D + 32
+    # (480 and 992: the one-row direct-to-LDS blocks)
+    (1, 2, 1, 150, 170, 288, True),
+    (1, 2, 2, 33, 200, 352, False),
+    (1, 2, 2, 100, 97, 480, False),
+    (1, 3, 1, 70, 130, 672, True),
+    (2, 2, 2, 65, 64, 992, False),
 ]
 
 

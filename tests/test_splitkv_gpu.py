@@ -66,6 +66,7 @@ PARTIAL = [
     (1, 2, 2, 100, 300, 512, False, "bf16", 17, 290),
     (1, 2, 2, 70, 200, 768, True, "bf16", 40, 200),      # split-D
     (1, 2, 1, 65, 130, 1024, False, "bf16", 31, 97),
+    (1, 2, 1, 65, 130, 416, True, "bf16", 31, 97),       # split-D at the layout of D + 32
     (1, 2, 2, 90, 170, 96, True, "bf16", 50, 120),       # tiled kernel
     (1, 2, 2, 80, 150, 128, True, "f32", 20, 140),
     (1, 2, 2, 120, 260, 128, False, "fp8", 45, 201),
