@@ -9,7 +9,7 @@
 
 #include "attn.h"
 #include "attn_common.h"
-#include "attn_launch.h"
+#include "attn_bwd.h"
 
 namespace {
 
@@ -390,8 +390,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                 need);
   if (dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "the backward pass takes bf16 only (dtype=%d)", dtype);
-  if (D != 64 && D != 128)
-    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the backward pass takes D = 64 or 128", (long long)D);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the backward pass takes D = 64, 128 or 256",
+                (long long)D);
   const int64_t lim = (int64_t)1 << 31;
   if (Nq * D * 2 >= lim || Nkv * D * 2 >= lim)
     return fail(ATTN_ERR_UNSUPPORTED, "a (batch, head) slab reaches 2^31 bytes");

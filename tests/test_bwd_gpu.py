@@ -57,6 +57,11 @@ CASES = [
     (1, 2, 2, 64, 64, 128, False),        # exactly one tile
     (1, 4, 4, 513, 513, 128, True),       # several query and key tiles on the diagonal
     (1, 2, 2, 300, 1, 64, True),          # one key
+    # D = 256 (its own dK/dV kernel)
+    (1, 2, 2, 200, 300, 256, True),
+    (2, 4, 2, 130, 257, 256, False),
+    (1, 2, 1, 333, 129, 256, True),
+    (1, 4, 4, 513, 513, 256, True),
 ]
 
 
@@ -77,8 +82,9 @@ def test_bwd_parity(case):
     assert (dq[:, :, ~seen] == 0).all(), "rows without keys must get dQ = 0"
 
 
-def test_bwd_deterministic():
-    w = Workload("bwd_det", 1, 4, 2, 300, 300, 128, True, "bf16", seed=5)
+@pytest.mark.parametrize("D", [128, 256])
+def test_bwd_deterministic(D):
+    w = Workload("bwd_det", 1, 4, 2, 300, 300, D, True, "bf16", seed=5)
     q, k, v = (t.cuda() for t in make_inputs(w))
     g = make_grad(w).cuda()
     O, L = A.fwd(q, k, v, causal=True, scale=w.scale)
@@ -109,10 +115,12 @@ def test_bwd_scale_variants():
                 assert rel_err(x, r) <= TOL, (sc, name, rel_err(x, r))
 
 
-def test_bwd_full_size_sampled():
-    """The benchmarked problem (B4 H32 N4096 D128, causal): every gradient of
-    three sampled heads against the oracle's per-head gradients."""
-    w = WORKLOADS["prefill_causal_bf16"]
+@pytest.mark.parametrize("name", ["prefill_causal_bf16", "causal_d256"])
+def test_bwd_full_size_sampled(name):
+    """The benchmarked problem (B4 H32 N4096 D128, causal) and a D = 256 one
+    (B1 H8 N4096, causal): every gradient of three sampled heads against the
+    oracle's per-head gradients."""
+    w = WORKLOADS[name] if name in WORKLOADS else Workload(name, 1, 8, 8, 4096, 4096, 256, True, "bf16")
     note(f"{w.name} backward, full size")
     (q, k, v, g), (dq, dk, dv) = run_bwd(w)
     rng = np.random.default_rng(2)
