@@ -75,28 +75,31 @@ _PIPE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_pipe.hip")
 # sources of the bf16 kernel of head dims 64 and 128
 _BF16 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_bf16.hip")
 _P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
+# the split-D kernels: four waves (D up to 960) and eight (D = 1024)
+_SPLITD = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_splitd.hip")
+_SPLITD8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_splitd8.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (_BF16, "3eca75bc6e411aea", 277459.21875 * 2 * 1024, 137317.703125 * 1024),
-    "gqa_causal_bf16": (_BF16, "3eca75bc6e411aea", 199771.0625 * 2 * 1024, 137221.09375 * 1024),
-    "gqa_cross_bf16": (_BF16, "3eca75bc6e411aea", 67881.5625 * 2 * 1024, 35328.0 * 1024),
-    "fp8_outlier": (_PIPE, "e207c00edc922816", 189905.09375 * 2 * 1024, 99840.0 * 1024),
+    "prefill_causal_bf16": (_BF16, "53fd85dcaa8ecb48", 281296.9375 * 2 * 1024, 137426.125 * 1024),
+    "gqa_causal_bf16": (_BF16, "53fd85dcaa8ecb48", 200326.65625 * 2 * 1024, 137227.375 * 1024),
+    "gqa_cross_bf16": (_BF16, "53fd85dcaa8ecb48", 67966.40625 * 2 * 1024, 35328.0 * 1024),
+    "fp8_outlier": (_PIPE, "b950ecf36dbe34db", 189491.90625 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
-    "fp8_blocks_outlier": (_PIPE, "e207c00edc922816", 187838.71875 * 2 * 1024, 99840.0 * 1024),
-    "splitd_bf16_d1024": (("attn_common.h", "attn_dma.h", "attn_fwd_splitd.hip"), "b1a4527d429ab446",
-                          164165.5 * 2 * 1024, 65664.0 * 1024),
+    "fp8_blocks_outlier": (_PIPE, "b950ecf36dbe34db", 188260.78125 * 2 * 1024, 99840.0 * 1024),
+    "splitd_bf16_d1024": (_SPLITD8, "dca91d739d485894", 163938.5 * 2 * 1024, 68142.9375 * 1024),
+    "splitd_bf16_d768": (_SPLITD, "c9934ca1a03d742f", 123049.5 * 2 * 1024, 49280.0 * 1024),
     "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
                          49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
-    "chunk_prefill_splitkv_bf16": (_BF16, "3eca75bc6e411aea", 73817.5625 * 2 * 1024, 33024.0 * 1024),
+    "chunk_prefill_splitkv_bf16": (_BF16, "53fd85dcaa8ecb48", 73817.6875 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
-    "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.hip"), "62725cf06fe17335",
-                        667898.9375 * 2 * 1024, 397492.28125 * 1024),
-    "fp8_p8_outlier": (_P8, "8da976182d1602e4", 172394.375 * 2 * 1024, 99840.0 * 1024),
-    "fp8_lean_outlier": (_P8, "8da976182d1602e4", 123132.03125 * 2 * 1024, 99840.0 * 1024),
-    "fp8_lean_causal_32k": (_P8, "8da976182d1602e4", 473900.53125 * 2 * 1024, 266242.203125 * 1024),
+    "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.h", "attn_bwd.hip"),
+                        "468bc9fc5083f9fe", 667925.3125 * 2 * 1024, 397464.21875 * 1024),
+    "fp8_p8_outlier": (_P8, "40c93540ee3a0f74", 169015.1875 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_outlier": (_P8, "40c93540ee3a0f74", 122964.25 * 2 * 1024, 99840.0 * 1024),
+    "fp8_lean_causal_32k": (_P8, "40c93540ee3a0f74", 440425.3125 * 2 * 1024, 266244.296875 * 1024),
 }
 
 
@@ -145,7 +148,7 @@ class ClockSampler:
             m = smi.amdsmi_get_gpu_metrics_info(self._handle)
             clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
             if clks:
-                return float(np.mean(clks))
+                return float(np.mean(clks))  # the XCDs' clocks (all busy under these kernels)
             c = m.get("current_gfxclk")
             if isinstance(c, (int, float)) and 0 < c < 10000:
                 return float(c)
@@ -160,7 +163,7 @@ class ClockSampler:
             try:
                 c = self._read()
                 if c is not None:
-                    self.samples.append(c)
+                    self.samples.append((time.perf_counter(), c))
             except Exception as e:  # pragma: no cover
                 self.error = f"amdsmi read failed: {type(e).__name__}"
                 return
@@ -183,14 +186,23 @@ class ClockSampler:
             except Exception:  # pragma: no cover
                 pass
 
-    def summary(self):
+    def summary(self, t0=None, t1=None):
+        """Median, min and max of the samples taken between t0 and t1
+        (perf_counter seconds: the timed loop), or of all of them if none
+        falls there.  Samples taken while the GPU idles between the warm-up
+        and the timed loop read the idle clock, hence the window."""
         if not self.samples:
             return None
-        s = np.asarray(self.samples)
+        t = np.asarray([a for a, _ in self.samples])
+        c = np.asarray([b for _, b in self.samples])
+        inside = (t >= t0) & (t <= t1) if t0 is not None and t1 is not None else np.ones(len(c), bool)
+        window = "the timed loop"
+        if not inside.any():
+            inside, window = np.ones(len(c), bool), "the last 0.5 s of warm-up and the timed loop"
+        s = c[inside]
         return {"median_mhz": round(float(np.median(s)), 1), "min_mhz": round(float(s.min()), 1),
                 "max_mhz": round(float(s.max()), 1), "samples": int(s.size),
-                "source": "amdsmi current gfx clock (mean over XCDs), sampled every 10 ms over the last "
-                          "0.5 s of warm-up and the timed loop"}
+                "source": f"amdsmi current gfx clock (mean over XCDs), sampled every 10 ms, over {window}"}
 
 
 def cpu_model():
@@ -453,7 +465,7 @@ def main():
     achieved = flops / avg_kernel_s / 1e12
     compute_dtype = "fp8" if w.dtype == "fp8blk" else w.dtype
     peak = PEAK_TFLOPS[compute_dtype]
-    sclk = clock.summary()
+    sclk = clock.summary(t0, t0 + wall)
     res = {
         "metric": METRIC_BWD if is_bwd(w) else METRIC,
         "value": round(value, 2),
