@@ -97,6 +97,7 @@ MEASURED_TRAFFIC = {
     # the whole backward step: prep + dK/dV + dQ launches
     "bwd_causal_bf16": (("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.h", "attn_bwd.hip"),
                         "468bc9fc5083f9fe", 667925.3125 * 2 * 1024, 397464.21875 * 1024),
+    "prefill_causal_bf16_poly": (_PIPE, "b950ecf36dbe34db", 266960.84375 * 2 * 1024, 133123.546875 * 1024),
     "fp8_p8_outlier": (_P8, "40c93540ee3a0f74", 169015.1875 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_outlier": (_P8, "40c93540ee3a0f74", 122964.25 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_causal_32k": (_P8, "40c93540ee3a0f74", 440425.3125 * 2 * 1024, 266244.296875 * 1024),
