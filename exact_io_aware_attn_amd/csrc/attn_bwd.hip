@@ -761,13 +761,471 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void attn_bwd_dq_kernel(BwdP
   }
 }
 
+// ---- D = 512: the work of one key (or query) block split between two waves --------
+// At D = 512 one wave's registers hold either the K rows or the V rows of its
+// 32 keys (128 registers each), and a dK^T or dV^T accumulator for the whole
+// head dim takes all 256 accumulation registers.  A work-group's four waves
+// therefore form two pairs over the same 32 keys.  The first wave of a pair
+// holds K, computes S = Q K^T, P = exp2(c S - lse2) (masked) and dV^T +=
+// dO^T P; the second holds V, computes dP = dO V^T, takes P from its partner
+// through LDS (float32, one barrier later), forms dS = P (dP - delta) and
+// dK^T += Q^T dS.  Each wave does the same number of products per tile (two
+// D-long contractions of a 32 x 32 block), and P is computed once.  Query
+// tiles are 32 rows (Q and dO of one tile are 64 KiB), two slots.
+
+template <int D>
+struct KVSplitCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 32 * NW / 2;         // keys per work-group, 32 per pair
+  static constexpr int BQ = 32;                  // query rows per LDS tile
+  static constexpr int RP = 2 * D;
+  static constexpr int NC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int TILE = BQ * RP;
+  static constexpr int DMA = TILE / 1024 / NW;
+  static constexpr int SLOT = 2 * TILE + 2 * BQ * 4;   // Q, dO, lse2, delta
+  static constexpr int XCH = (NW / 2) * 64 * 16 * 4;   // P of each pair: 16 floats per lane
+  static constexpr int LDS = 2 * SLOT + XCH;
+  static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(2 * BQ <= NT, "one thread per lse2 / delta value");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p) {
+  using C = KVSplitCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave & 1;   // 0: K, S, P, dV;  1: V, dP, dS, dK
+  const int pair = wave >> 1;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int g16 = lane >> 4, r16 = lane & 15;
+
+  const int n_kt = (p.Nkv + C::BK - 1) / C::BK;
+  const int nslot = p.pair_kv ? (n_kt + 1) / 2 : n_kt;
+  const int wg = xcd_remap(blockIdx.x, nslot * p.B * p.Hkv);
+  const int slot_k = wg % nslot;
+  const int bh = wg / nslot;
+  const int hk = bh % p.Hkv;
+  const int b = bh / p.Hkv;
+  const int njobs = (p.pair_kv && 2 * slot_k + 1 != n_kt) ? 2 : 1;
+  for (int job = 0; job < njobs; ++job) {
+  if (job > 0) __syncthreads();
+  const int kt = job == 0 ? slot_k : n_kt - 1 - slot_k;
+  const int k0 = kt * C::BK;
+  const int k0w = k0 + 32 * pair;
+  const int key = k0w + l32;
+
+  // this wave's K (role 0) or V (role 1) rows in B-operand layout
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const __amdgpu_buffer_rsrc_t rr =
+      make_rsrc((const __bf16*)(role ? p.v : p.k) + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  u32x4 reg[C::NC];
+#pragma unroll
+  for (int cc = 0; cc < C::NC; ++cc) reg[cc] = buf_load16(rr, (uint32_t)(key * C::RP + (2 * cc + h) * 16));
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    acc[db] = f32x16{};
+    hold_acc(acc[db]);
+  }
+
+  const int xr = rt_swz<D>(l32);
+  const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
+  const int xlo = rt_swz<D>(rlo), xhi = rt_swz<D>(rhi);
+  const int cpart = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int rbase = l32 * C::RP;
+  const int tbase_lo = rlo * C::RP + ((r16 & 1) << 3), tbase_hi = rhi * C::RP + ((r16 & 1) << 3);
+  auto rowfrag = [&](const char* tile, int cc) {
+    const int chunk = (2 * cc + h) ^ opaque_i(xr);
+    return lds_load16(tile, (uint32_t)(rbase + (chunk << 4)));
+  };
+  auto trfrag = [&](const char* tile, int r0, int db) {
+    const int chunk = 4 * db + cpart;
+    const uint32_t lo_a = (uint32_t)(tbase_lo + r0 * C::RP + ((chunk ^ opaque_i(xlo)) << 4));
+    const uint32_t hi_a = (uint32_t)(tbase_hi + r0 * C::RP + ((chunk ^ opaque_i(xhi)) << 4));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + lo_a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + hi_a));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+
+  const int kv_off = p.Nkv - p.Nq;
+  const int n_qt = (p.Nq + C::BQ - 1) / C::BQ;
+  const int qt0 = p.causal ? min(max(0, k0 - kv_off) / C::BQ, n_qt) : 0;
+  const int nq = n_qt - qt0;
+  const int T = p.group * nq;
+  const float c = p.scale * kLog2e;
+
+  uint32_t voff[C::DMA];
+  dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
+  auto q_row0 = [&](int t) { return (int64_t)b * p.Hq + hk * p.group + t / nq; };
+  auto issue = [&](int t, int slot) {
+    const int q0 = (qt0 + t % nq) * C::BQ;
+    const int64_t slab = q_row0(t) * (int64_t)p.Nq * D;
+    const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
+    const i32x4 rq = sgpr_rsrc((const __bf16*)p.q + slab, (uint32_t)(p.Nq * C::RP));
+    const i32x4 ro = sgpr_rsrc((const __bf16*)p.dout + slab, (uint32_t)(p.Nq * C::RP));
+    dma_blocks<C::DMA>(rsrc_at(rq, (uint32_t)(q0 * C::RP)), dst, voff, wave);
+    dma_blocks<C::DMA>(rsrc_at(ro, (uint32_t)(q0 * C::RP)), dst + C::TILE, voff, wave);
+  };
+  float st_l = 0.0f;
+  auto load_ld = [&](int t) {
+    if (tid < 2 * C::BQ) {
+      const int r = (qt0 + t % nq) * C::BQ + (tid % C::BQ);
+      const int64_t row = q_row0(t) * (int64_t)p.Nq + r;
+      const bool live = r < p.Nq;
+      st_l = tid < C::BQ ? (live ? p.lse2[row] : INFINITY) : (live ? p.delta[row] : 0.0f);
+    }
+  };
+  auto store_ld = [&](int slot) {
+    if (tid < 2 * C::BQ) reinterpret_cast<float*>(lds + slot * C::SLOT + 2 * C::TILE)[tid] = st_l;
+  };
+  // the pair's P: register r of lane l at float 4 (64 (r / 4) + l) + r % 4
+  float* const xch = reinterpret_cast<float*>(lds + 2 * C::SLOT) + pair * (64 * 16);
+
+  if (T > 0) {
+    issue(0, 0);
+    load_ld(0);
+    store_ld(0);
+  }
+  for (int t = 0; t < T; ++t) {
+    const int slot = t & 1;
+    const int q0 = (qt0 + t % nq) * C::BQ;
+    wait_vmem_all();
+    __syncthreads();  // tile t resident; the other slot (tile t-1) and xch are free
+    if (t + 1 < T) {
+      issue(t + 1, slot ^ 1);
+      load_ld(t + 1);
+    }
+    const char* const tQ = lds + slot * C::SLOT;
+    const char* const tO = tQ + C::TILE;
+    const float* const tL = reinterpret_cast<const float*>(tQ + 2 * C::TILE);
+    const float* const tD = tL + C::BQ;
+    const char* const tR = role ? tO : tQ;   // row operand of S or dP
+    const char* const tT = role ? tQ : tO;   // transposed operand of dK^T or dV^T
+
+    // S (role 0) or dP (role 1): 32 query rows x the pair's 32 keys.  One
+    // wave per SIMD has no other wave to hide LDS latency behind, so the
+    // row fragments are read W products ahead and the transposed fragments
+    // of the dV^T / dK^T products W2 ahead (fragment j in slot j % W);
+    // scheduling fences keep the compiler from sinking each read to just
+    // before its product.
+    constexpr int W = 4, W2 = 4, NS = 2 * C::NDB;
+    f32x16 x = f32x16{};
+    u32x4 f[W], tf[W2];
+    static_for<0, W>([&](auto iI) {
+      constexpr int i = decltype(iI)::value;
+      f[i] = rowfrag(tR, i);
+    });
+    static_for<0, C::NC>([&](auto cI) {
+      constexpr int cc = decltype(cI)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      x = mfma_bf16(f[cc % W], reg[cc], x);
+      if constexpr (cc + W < C::NC) f[cc % W] = rowfrag(tR, cc + W);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    // step j of the second products: (kc, db) = (j / NDB, j % NDB); their
+    // operands do not depend on P
+    static_for<0, W2>([&](auto jI) {
+      constexpr int j = decltype(jI)::value;
+      tf[j] = trfrag(tT, 16 * (j / C::NDB), j % C::NDB);
+    });
+    if (role == 0) {
+      const bool mask = p.causal && q0 + kv_off < k0w + 31;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + 8 * g + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e = exp2_fast(__builtin_fmaf(x[4 * g + i], c, -l4[i]));
+          if (mask && key > q0 + 8 * g + 4 * h + i + kv_off) e = 0.0f;
+          x[4 * g + i] = e;
+        }
+        *reinterpret_cast<f32x4*>(xch + 4 * (64 * g + lane)) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+      }
+    }
+    __syncthreads();  // P of the pair visible to its second wave
+    u32x4 fr[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float v[4];
+      if (role == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = x[4 * g + i];
+      } else {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(xch + 4 * (64 * g + lane));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(tD + 8 * g + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = p4[i] * (x[4 * g + i] - d4[i]);
+      }
+      const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
+      if (g & 1) {
+        fr[g >> 1].z = w0;
+        fr[g >> 1].w = w1;
+      } else {
+        fr[g >> 1].x = w0;
+        fr[g >> 1].y = w1;
+      }
+    }
+    // dV^T += dO^T P (role 0), dK^T += Q^T dS (role 1)
+    static_for<0, NS>([&](auto jI) {
+      constexpr int j = decltype(jI)::value;
+      constexpr int kc = j / C::NDB, db = j % C::NDB;
+      __builtin_amdgcn_sched_barrier(0);
+      acc[db] = mfma_bf16(tf[j % W2], fr[kc], acc[db]);
+      hold_acc(acc[db]);
+      if constexpr (j + W2 < NS) tf[j % W2] = trfrag(tT, 16 * ((j + W2) / C::NDB), (j + W2) % C::NDB);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < T) store_ld(slot ^ 1);
+  }
+
+  if (key < p.Nkv) {
+    const int64_t row = kv_slab + (int64_t)key * D;
+    void* const out = role ? p.dk : p.dv;
+    const float f = role ? p.scale : 1.0f;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * h;
+        store_o4(out, false, row + d, acc[db][4 * g + 0] * f, acc[db][4 * g + 1] * f, acc[db][4 * g + 2] * f,
+                 acc[db][4 * g + 3] * f);
+      }
+    }
+  }
+}  // job
+}
+
+// dQ at D = 512: pairs of waves over the same 32 query rows.  The first wave
+// holds the Q rows and computes S^T = K Q^T and P^T, the second holds the dO
+// rows and computes dP^T = V dO^T; they swap the two through LDS (float32),
+// both form dS^T = P^T (dP^T - delta) from the same values, and each
+// accumulates one half of dQ^T += K^T dS^T (d below or above D / 2).  Key
+// tiles are 32 keys (K and V of one tile are 64 KiB), two slots.
+
+template <int D>
+struct QSplitCfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = 32 * NW / 2;         // query rows per work-group, 32 per pair
+  static constexpr int BC = 32;                  // keys per LDS tile
+  static constexpr int RP = 2 * D;
+  static constexpr int NC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int HDB = NDB / 2;            // dQ^T blocks per wave
+  static constexpr int TILE = BC * RP;
+  static constexpr int DMA = TILE / 1024 / NW;
+  static constexpr int SLOT = 2 * TILE;          // K, V
+  static constexpr int XCH = NW * 64 * 16 * 4;   // each wave's S or dP block
+  static constexpr int LDS = 2 * SLOT + XCH;
+  static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) {
+  using C = QSplitCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const uint32_t lds_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave & 1;   // 0: Q, S, P;  1: dO, dP
+  const int pair = wave >> 1;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int g16 = lane >> 4, r16 = lane & 15;
+
+  const int n_qt = (p.Nq + C::BR - 1) / C::BR;
+  const int wg = xcd_remap(blockIdx.x, n_qt * p.B * p.Hq);
+  const int qt_raw = wg % n_qt;
+  const int bh = wg / n_qt;
+  const int hq = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int qt = p.causal ? n_qt - 1 - qt_raw : qt_raw;
+  const int hk = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int q0w = q0 + 32 * pair;
+  const int qrow = q0w + l32;
+
+  const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq;
+  const __amdgpu_buffer_rsrc_t rr =
+      make_rsrc((const __bf16*)(role ? p.dout : p.q) + q_slab * D, (uint32_t)(p.Nq * C::RP));
+  u32x4 reg[C::NC];
+#pragma unroll
+  for (int cc = 0; cc < C::NC; ++cc) reg[cc] = buf_load16(rr, (uint32_t)(qrow * C::RP + (2 * cc + h) * 16));
+  const bool live = qrow < p.Nq;
+  const float lq = live ? p.lse2[q_slab + qrow] : INFINITY;
+  const float dq_row = live ? p.delta[q_slab + qrow] : 0.0f;
+
+  f32x16 acc[C::HDB];
+#pragma unroll
+  for (int db = 0; db < C::HDB; ++db) {
+    acc[db] = f32x16{};
+    hold_acc(acc[db]);
+  }
+
+  const int kv_off = p.Nkv - p.Nq;
+  int kv_end = p.Nkv;
+  if (p.causal) kv_end = min(p.Nkv, min(q0 + C::BR, p.Nq) + kv_off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
+  const int klim = p.causal ? min(p.Nkv - 1, qrow + kv_off) : p.Nkv - 1;  // last visible key
+  const float c = p.scale * kLog2e;
+
+  const int xr = rt_swz<D>(l32);
+  const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
+  const int xlo = rt_swz<D>(rlo), xhi = rt_swz<D>(rhi);
+  const int cpart = 2 * (g16 & 1) + ((r16 & 3) >> 1);
+  const int rbase = l32 * C::RP;
+  const int tbase_lo = rlo * C::RP + ((r16 & 1) << 3), tbase_hi = rhi * C::RP + ((r16 & 1) << 3);
+  auto rowfrag = [&](const char* tile, int cc) {
+    const int chunk = (2 * cc + h) ^ opaque_i(xr);
+    return lds_load16(tile, (uint32_t)(rbase + (chunk << 4)));
+  };
+  auto trfrag = [&](const char* tile, int r0, int db) {
+    const int chunk = 4 * db + cpart;
+    const uint32_t lo_a = (uint32_t)(tbase_lo + r0 * C::RP + ((chunk ^ opaque_i(xlo)) << 4));
+    const uint32_t hi_a = (uint32_t)(tbase_hi + r0 * C::RP + ((chunk ^ opaque_i(xhi)) << 4));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + lo_a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + hi_a));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+
+  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
+  const i32x4 rk = sgpr_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  const i32x4 rv = sgpr_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
+  uint32_t voff[C::DMA];
+  dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
+  auto issue = [&](int kt, int slot) {
+    const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
+    dma_blocks<C::DMA>(rsrc_at(rk, (uint32_t)(kt * C::TILE)), dst, voff, wave);
+    dma_blocks<C::DMA>(rsrc_at(rv, (uint32_t)(kt * C::TILE)), dst + C::TILE, voff, wave);
+  };
+  // each wave's block: register r of lane l at float 4 (64 (r / 4) + l) + r % 4
+  float* const mine = reinterpret_cast<float*>(lds + 2 * C::SLOT) + wave * (64 * 16);
+  const float* const other = reinterpret_cast<const float*>(lds + 2 * C::SLOT) + (wave ^ 1) * (64 * 16);
+
+  if (n_kt > 0) issue(0, 0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int slot = kt & 1;
+    wait_vmem_all();
+    __syncthreads();  // tile kt resident; the other slot and the exchange are free
+    if (kt + 1 < n_kt) issue(kt + 1, slot ^ 1);
+    const int key0 = kt * C::BC;
+    // uniform over the pair: its rows see none of the tile (the barriers
+    // below are still taken)
+    const bool skip = p.causal && key0 > q0w + 31 + kv_off;
+    const char* const tK = lds + slot * C::SLOT;
+    const char* const tV = tK + C::TILE;
+    const bool mask = key0 + C::BC > p.Nkv || (p.causal && key0 + C::BC - 1 > q0w + kv_off);
+
+    // fragment reads run ahead of the products as in the dK/dV kernel
+    constexpr int W = 4, W2 = 4, NS = 2 * C::HDB;
+    f32x16 x = f32x16{};
+    u32x4 tf[W2];
+    if (!skip) {
+      const char* const tR = role ? tV : tK;
+      u32x4 f[W];
+      static_for<0, W>([&](auto iI) {
+        constexpr int i = decltype(iI)::value;
+        f[i] = rowfrag(tR, i);
+      });
+      static_for<0, C::NC>([&](auto cI) {
+        constexpr int cc = decltype(cI)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        x = mfma_bf16(f[cc % W], reg[cc], x);
+        if constexpr (cc + W < C::NC) f[cc % W] = rowfrag(tR, cc + W);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      // step j of dQ^T += K^T dS^T: (kc, db) = (j / HDB, role HDB + j % HDB)
+      static_for<0, W2>([&](auto jI) {
+        constexpr int j = decltype(jI)::value;
+        tf[j] = trfrag(tK, 16 * (j / C::HDB), role * C::HDB + j % C::HDB);
+      });
+      if (role == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = exp2_fast(__builtin_fmaf(x[r], c, -lq));
+          if (mask && key0 + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
+          x[r] = e;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(mine + 4 * (64 * g + lane)) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+    }
+    __syncthreads();  // both blocks of each pair visible
+    if (!skip) {
+      u32x4 fr[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(other + 4 * (64 * g + lane));
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = role ? y[i] : x[4 * g + i];
+          const float dpv = role ? x[4 * g + i] : y[i];
+          v[i] = pv * (dpv - dq_row);
+        }
+        const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
+        if (g & 1) {
+          fr[g >> 1].z = w0;
+          fr[g >> 1].w = w1;
+        } else {
+          fr[g >> 1].x = w0;
+          fr[g >> 1].y = w1;
+        }
+      }
+      static_for<0, NS>([&](auto jI) {
+        constexpr int j = decltype(jI)::value;
+        constexpr int kc = j / C::HDB, db = j % C::HDB;
+        __builtin_amdgcn_sched_barrier(0);
+        acc[db] = mfma_bf16(tf[j % W2], fr[kc], acc[db]);
+        hold_acc(acc[db]);
+        if constexpr (j + W2 < NS)
+          tf[j % W2] = trfrag(tK, 16 * ((j + W2) / C::HDB), role * C::HDB + (j + W2) % C::HDB);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (live) {
+    const int64_t row = (q_slab + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < C::HDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = (role * C::HDB + db) * 32 + 8 * g + 4 * h;
+        store_o4(p.dq, false, row + d, acc[db][4 * g + 0] * p.scale, acc[db][4 * g + 1] * p.scale,
+                 acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch(const BwdParams& p0, hipStream_t stream) {
+  // D = 512 runs the kernels that split each block between two waves
+  constexpr bool split = D > 256;
+  constexpr int BK = split ? KVSplitCfg<D>::BK : KVCfg<D>::BK;
+  constexpr int BR = split ? QSplitCfg<D>::BR : QCfg<D>::BR;
   BwdParams p = p0;
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   const int64_t prep_wg = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
-  const int n_kt = (p.Nkv + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
-  const int n_qt = (p.Nq + QCfg<D>::BR - 1) / QCfg<D>::BR;
+  const int n_kt = (p.Nkv + BK - 1) / BK;
+  const int n_qt = (p.Nq + BR - 1) / BR;
   p.pair_kv = pair_causal_grid(p.causal, (int64_t)p.B * p.Hkv, n_kt, p.Nq, p.Nkv);
   const int64_t kv_wg = (int64_t)(p.pair_kv ? (n_kt + 1) / 2 : n_kt) * p.B * p.Hkv;
   const int64_t q_wg = (int64_t)n_qt * p.B * p.Hq;
@@ -776,13 +1234,18 @@ hipError_t launch(const BwdParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)prep_wg), dim3(256), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if constexpr (D <= 128)
+  if constexpr (split)
+    hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<D>), dim3((unsigned)kv_wg), dim3(KVSplitCfg<D>::NT), 0, stream, p);
+  else if constexpr (D <= 128)
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
   else
     hipLaunchKernelGGL((attn_bwd_dkdv_wide_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)q_wg), dim3(QCfg<D>::NT), 0, stream, p);
+  if constexpr (split)
+    hipLaunchKernelGGL((attn_bwd_dq_split_kernel<D>), dim3((unsigned)q_wg), dim3(QSplitCfg<D>::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)q_wg), dim3(QCfg<D>::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -793,6 +1256,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     case 64: return launch<64>(p, stream);
     case 128: return launch<128>(p, stream);
     case 256: return launch<256>(p, stream);
+    case 512: return launch<512>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

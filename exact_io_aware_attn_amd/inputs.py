@@ -109,6 +109,10 @@ WORKLOADS = {
     # dV from Q, K, V, the forward O and LSE and an upstream dO
     "bwd_causal_bf16": Workload("bwd_causal_bf16", 4, 32, 32, 4096, 4096, 128, True, "bf16",
                                 extra={"pass": "bwd"}),
+    # the backward at D = 512 (the kernels that split each block between two
+    # waves), causal self-attention, 32 heads of 4096 tokens
+    "bwd_causal_bf16_d512": Workload("bwd_causal_bf16_d512", 1, 32, 32, 4096, 4096, 512, True, "bf16",
+                                     extra={"pass": "bwd"}),
     # chunked prefill: a 256-token chunk against a 32K-token context, GQA,
     # causal (bottom-right: the chunk sees the whole context and itself
     # causally).  B * Hq * query tiles = 64 work-groups for 256 CUs, the case

@@ -330,11 +330,11 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq);
  *   o, lse         : the forward outputs for the same q, k, v, causal, scale
  *   workspace      : DEVICE, 16-byte aligned, >= attn_bwd_workspace_bytes;
  *                    overwritten (the library allocates nothing)
- *   dtype          : ATTN_BF16 only; D = 64, 128 or 256; causal and scale as
+ *   dtype          : ATTN_BF16 only; D = 64, 128, 256 or 512; causal and scale as
  *                    attn_fwd (any finite scale).
  * Outputs are overwritten (not accumulated into).  float32 accumulation;
- * every key's dK/dV and every row's dQ is computed by one wave, without
- * atomics, so results are deterministic.  Three kernels on `stream`.
+ * every output element is accumulated by one wave, without atomics, so
+ * results are deterministic.  Three kernels on `stream`.
  * Errors: ATTN_ERR_INVALID_ARG (NULL, sizes, alignment, workspace size),
  * ATTN_ERR_UNSUPPORTED (dtype, D, sizes past 2^31), ATTN_ERR_HIP.
  */
