@@ -837,22 +837,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
     hold_acc(acc[db]);
   }
 
+  // Per-lane LDS offsets.  The swizzle keys are below 16, so they change only
+  // the low four bits of a chunk index: row fragment cc (chunk 2 cc + h) is
+  // one of eight per-lane offsets plus 256 (cc / 8) bytes, and a transposed
+  // read of block db (chunk 4 db + cpart) one of four plus 256 (db / 4), the
+  // constants going into the instructions' offset fields.
   const int xr = rt_swz<D>(l32);
   const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
   const int xlo = rt_swz<D>(rlo), xhi = rt_swz<D>(rhi);
   const int cpart = 2 * (g16 & 1) + ((r16 & 3) >> 1);
-  const int rbase = l32 * C::RP;
-  const int tbase_lo = rlo * C::RP + ((r16 & 1) << 3), tbase_hi = rhi * C::RP + ((r16 & 1) << 3);
-  auto rowfrag = [&](const char* tile, int cc) {
-    const int chunk = (2 * cc + h) ^ opaque_i(xr);
-    return lds_load16(tile, (uint32_t)(rbase + (chunk << 4)));
-  };
+  uint32_t ro[8], tlo[4], thi[4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) ro[m] = (uint32_t)(l32 * C::RP + (((2 * m + h) ^ xr) << 4));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    tlo[m] = (uint32_t)(rlo * C::RP + ((r16 & 1) << 3) + (((4 * m + cpart) ^ xlo) << 4));
+    thi[m] = (uint32_t)(rhi * C::RP + ((r16 & 1) << 3) + (((4 * m + cpart) ^ xhi) << 4));
+  }
+  auto rowfrag = [&](const char* tile, int cc) { return lds_load16(tile, ro[cc % 8] + 256 * (cc / 8)); };
   auto trfrag = [&](const char* tile, int r0, int db) {
-    const int chunk = 4 * db + cpart;
-    const uint32_t lo_a = (uint32_t)(tbase_lo + r0 * C::RP + ((chunk ^ opaque_i(xlo)) << 4));
-    const uint32_t hi_a = (uint32_t)(tbase_hi + r0 * C::RP + ((chunk ^ opaque_i(xhi)) << 4));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + lo_a));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + hi_a));
+    const uint32_t k = (uint32_t)(256 * (db / 4) + r0 * C::RP);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + tlo[db % 4] + k));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + thi[db % 4] + k));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2.x, l2.y, h2.x, h2.y};
   };
@@ -938,6 +944,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
       constexpr int j = decltype(jI)::value;
       tf[j] = trfrag(tT, 16 * (j / C::NDB), j % C::NDB);
     });
+    float pv[16];  // P (role 0)
     if (role == 0) {
       const bool mask = p.causal && q0 + kv_off < k0w + 31;
 #pragma unroll
@@ -947,9 +954,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
         for (int i = 0; i < 4; ++i) {
           float e = exp2_fast(__builtin_fmaf(x[4 * g + i], c, -l4[i]));
           if (mask && key > q0 + 8 * g + 4 * h + i + kv_off) e = 0.0f;
-          x[4 * g + i] = e;
+          pv[4 * g + i] = e;
         }
-        *reinterpret_cast<f32x4*>(xch + 4 * (64 * g + lane)) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(xch + 4 * (64 * g + lane)) =
+            f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
       }
     }
     __syncthreads();  // P of the pair visible to its second wave
@@ -959,7 +967,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
       float v[4];
       if (role == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = x[4 * g + i];
+        for (int i = 0; i < 4; ++i) v[i] = pv[4 * g + i];
       } else {
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(xch + 4 * (64 * g + lane));
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(tD + 8 * g + 4 * h);
@@ -1083,22 +1091,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
   const int klim = p.causal ? min(p.Nkv - 1, qrow + kv_off) : p.Nkv - 1;  // last visible key
   const float c = p.scale * kLog2e;
 
+  // Per-lane LDS offsets.  The swizzle keys are below 16, so they change only
+  // the low four bits of a chunk index: row fragment cc (chunk 2 cc + h) is
+  // one of eight per-lane offsets plus 256 (cc / 8) bytes, and a transposed
+  // read of block db (chunk 4 db + cpart) one of four plus 256 (db / 4), the
+  // constants going into the instructions' offset fields.
   const int xr = rt_swz<D>(l32);
   const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
   const int xlo = rt_swz<D>(rlo), xhi = rt_swz<D>(rhi);
   const int cpart = 2 * (g16 & 1) + ((r16 & 3) >> 1);
-  const int rbase = l32 * C::RP;
-  const int tbase_lo = rlo * C::RP + ((r16 & 1) << 3), tbase_hi = rhi * C::RP + ((r16 & 1) << 3);
-  auto rowfrag = [&](const char* tile, int cc) {
-    const int chunk = (2 * cc + h) ^ opaque_i(xr);
-    return lds_load16(tile, (uint32_t)(rbase + (chunk << 4)));
-  };
+  uint32_t ro[8], tlo[4], thi[4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) ro[m] = (uint32_t)(l32 * C::RP + (((2 * m + h) ^ xr) << 4));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    tlo[m] = (uint32_t)(rlo * C::RP + ((r16 & 1) << 3) + (((4 * m + cpart) ^ xlo) << 4));
+    thi[m] = (uint32_t)(rhi * C::RP + ((r16 & 1) << 3) + (((4 * m + cpart) ^ xhi) << 4));
+  }
+  auto rowfrag = [&](const char* tile, int cc) { return lds_load16(tile, ro[cc % 8] + 256 * (cc / 8)); };
   auto trfrag = [&](const char* tile, int r0, int db) {
-    const int chunk = 4 * db + cpart;
-    const uint32_t lo_a = (uint32_t)(tbase_lo + r0 * C::RP + ((chunk ^ opaque_i(xlo)) << 4));
-    const uint32_t hi_a = (uint32_t)(tbase_hi + r0 * C::RP + ((chunk ^ opaque_i(xhi)) << 4));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + lo_a));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + hi_a));
+    const uint32_t k = (uint32_t)(256 * (db / 4) + r0 * C::RP);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + tlo[db % 4] + k));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + thi[db % 4] + k));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2.x, l2.y, h2.x, h2.y};
   };
@@ -1134,6 +1148,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
     // fragment reads run ahead of the products as in the dK/dV kernel
     constexpr int W = 4, W2 = 4, NS = 2 * C::HDB;
     f32x16 x = f32x16{};
+    float xv[16];
     u32x4 tf[W2];
     if (!skip) {
       const char* const tR = role ? tV : tK;
@@ -1154,17 +1169,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
         constexpr int j = decltype(jI)::value;
         tf[j] = trfrag(tK, 16 * (j / C::HDB), role * C::HDB + j % C::HDB);
       });
+      // role 0: P; role 1: dP as it stands
       if (role == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float e = exp2_fast(__builtin_fmaf(x[r], c, -lq));
           if (mask && key0 + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
-          x[r] = e;
+          xv[r] = e;
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xv[r] = x[r];
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(mine + 4 * (64 * g + lane)) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(mine + 4 * (64 * g + lane)) =
+            f32x4{xv[4 * g], xv[4 * g + 1], xv[4 * g + 2], xv[4 * g + 3]};
     }
     __syncthreads();  // both blocks of each pair visible
     if (!skip) {
@@ -1173,11 +1193,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
       for (int g = 0; g < 4; ++g) {
         const f32x4 y = *reinterpret_cast<const f32x4*>(other + 4 * (64 * g + lane));
         float v[4];
+        if (role == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = role ? y[i] : x[4 * g + i];
-          const float dpv = role ? x[4 * g + i] : y[i];
-          v[i] = pv * (dpv - dq_row);
+          for (int i = 0; i < 4; ++i) v[i] = xv[4 * g + i] * (y[i] - dq_row);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = y[i] * (xv[4 * g + i] - dq_row);
         }
         const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
         if (g & 1) {

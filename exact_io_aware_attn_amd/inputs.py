@@ -109,8 +109,10 @@ WORKLOADS = {
     # dV from Q, K, V, the forward O and LSE and an upstream dO
     "bwd_causal_bf16": Workload("bwd_causal_bf16", 4, 32, 32, 4096, 4096, 128, True, "bf16",
                                 extra={"pass": "bwd"}),
-    # the backward at D = 512 (the kernels that split each block between two
-    # waves), causal self-attention, 32 heads of 4096 tokens
+    # the backward at D = 256 and 512, causal self-attention over 4096
+    # tokens, with the flops of the D = 128 problem
+    "bwd_causal_bf16_d256": Workload("bwd_causal_bf16_d256", 2, 32, 32, 4096, 4096, 256, True, "bf16",
+                                     extra={"pass": "bwd"}),
     "bwd_causal_bf16_d512": Workload("bwd_causal_bf16_d512", 1, 32, 32, 4096, 4096, 512, True, "bf16",
                                      extra={"pass": "bwd"}),
     # chunked prefill: a 256-token chunk against a 32K-token context, GQA,

@@ -41,7 +41,7 @@ KNOWN_SCRATCH = {
     ("attn_bwd.hip", "attn_bwd_dq_kernelILi256E"): 108,
     # D = 512 dK/dV: the same, before and after each query-tile loop, plus one
     # dword reloaded per tile
-    ("attn_bwd.hip", "attn_bwd_dkdv_split_kernelILi512E"): 144,
+    ("attn_bwd.hip", "attn_bwd_dkdv_split_kernelILi512E"): 204,
 }
 
 SCALAR_WRITE = re.compile(r"\bs_(store|buffer_store|scratch_store|dcache_wb|dcache_discard|atomic|buffer_atomic)")
