@@ -1,5 +1,5 @@
-// attn_bwd.hip -- exact attention backward on gfx950 (bf16, D = 64, 128 and
-// 256).
+// attn_bwd.hip -- exact attention backward on gfx950 (bf16, D = 64, 128, 256
+// and 512).
 //
 // FlashAttention summary page, method paragraph: the backward pass recomputes
 // S = Q K^T instead of storing it; FlashAttention v1/v2/v3/v4 blog post,
@@ -15,34 +15,32 @@
 //   * prep: delta_i = dO_i . O_i in float32 and lse2_i = LSE_i log2(e)
 //     (+inf for a row that saw no key, so that its P is 0), into a
 //     caller-owned workspace;
-//   * dK/dV: one work-group per (batch, KV head, 128 keys), 32 keys per wave
-//     held in registers with the wave's dK^T and dV^T accumulators; Q and dO
-//     tiles of 64 rows of every query head of the group stream through LDS.
-//     S = Q K^T and dP = dO V^T put one key per lane (column) and 16 query
-//     rows per lane in the accumulator registers, which rounded to bf16 are
-//     the B operands of dV^T += dO^T P and dK^T += Q^T dS as they stand; the
-//     A operands dO^T and Q^T come from the transposing LDS read.  No
-//     atomics: each key's gradients are owned by one wave.
-//   * dQ: one work-group per (batch, query head, 128 rows), the forward
-//     pass's layout: Q and dO rows in registers (one query per lane), K and V
-//     tiles of 64 keys in LDS; S^T = K Q^T, dP^T = V dO^T, then
+//   * dK/dV: the keys of a (batch, KV head) in blocks of 32 per wave, held in
+//     registers with the wave's dK^T and dV^T accumulators; Q and dO tiles of
+//     every query head of the group stream through LDS.  S = Q K^T and dP =
+//     dO V^T put one key per lane (column) and 16 query rows per lane in the
+//     accumulator registers, which rounded to bf16 are the B operands of
+//     dV^T += dO^T P and dK^T += Q^T dS as they stand; the A operands dO^T
+//     and Q^T come from the transposing LDS read.  No atomics: each key's
+//     gradients are owned by one wave.
+//   * dQ: the forward pass's layout, query rows in registers (one query per
+//     lane), K and V tiles in LDS; S^T = K Q^T, dP^T = V dO^T, then
 //     dQ^T += K^T dS^T with K^T from the transposing read.
 // S and dP are recomputed in both the dK/dV and the dQ launch (seven matrix
 // products where five would do with atomic dQ accumulation): the results
 // are deterministic.
 //
+// D = 64 and 128: one wave holds both K and V of its keys (dK/dV, 128 keys
+// and one wave per SIMD per work-group, 64-row Q/dO tiles) or both Q and dO
+// of its rows (dQ, 128 rows, two waves per SIMD, 64-key K/V tiles).  D = 256
+// and 512: those registers no longer fit, and the work of each block is
+// split between the two waves of a pair (the split kernels below).
+//
 // Q/dO and K/V tiles stream into LDS with direct-to-LDS buffer loads, two
 // slots, one barrier per tile (the next tile's loads are issued right after
 // it).  Their rows are read both as row fragments (16 rows of one 16-byte
 // chunk per LDS phase) and through ds_read_b64_tr_b16 (4 rows x 4 chunks per
-// phase); the XOR swizzle rt_swz keeps both conflict-free at D = 128.  The
-// dK/dV kernel runs one wave per SIMD (its accumulators take 2 D registers
-// per lane); the dQ kernel runs two.  D = 256 has its own dK/dV kernel (the
-// same products without the two-block pipeline, its registers being full)
-// and runs the dQ kernel at one wave per SIMD, with register placement left
-// to the compiler (pinning that kernel's Q/dO fragments or its dQ^T
-// accumulators to accumulation registers with empty inline asm gave wrong
-// dQ values on the device; the cause was not found, so neither is done).
+// phase); the XOR swizzle rt_swz keeps both conflict-free.
 #include "attn_common.h"
 #include "attn_dma.h"
 #include "attn_bwd.h"
@@ -78,14 +76,6 @@ __device__ __forceinline__ void hold_acc(f32x16& x) { asm volatile("" : "+a"(x))
 // The same for an operand fragment that stays live for the whole kernel
 // (the MFMA reads its A/B operands from accumulation registers as well).
 __device__ __forceinline__ void hold_frag(u32x4& x) { asm volatile("" : "+a"(x)); }
-
-// A copy of x the optimiser cannot see through: what is computed from it is
-// formed where it is used instead of being hoisted out of the loop into
-// registers (at D = 256 every register is taken).
-__device__ __forceinline__ int opaque_i(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
@@ -408,208 +398,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 }  // job
 }
 
-// ---- dK, dV at D = 256 -------------------------------------------------------------
-// The same products and operand layouts as above, with the registers of D =
-// 256: a wave's K and V rows take 128 VGPRs and its dK^T and dV^T
-// accumulators all 256 AGPRs, which leaves no room for the two-block software
-// pipeline.  Each query tile's two 32-row blocks run one after the other (S
-// and dP; the softmax and dS; the dV and dK products), the lse2/delta values
-// are read from LDS where they are used, and every fragment address is formed
-// at its read from the lane's swizzle keys.
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_wide_kernel(BwdParams p) {
-  using C = KVCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
-  const uint32_t lds_base =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
-  const int g16 = lane >> 4, r16 = lane & 15;
-
-  const int n_kt = (p.Nkv + C::BK - 1) / C::BK;
-  const int nslot = p.pair_kv ? (n_kt + 1) / 2 : n_kt;
-  const int wg = xcd_remap(blockIdx.x, nslot * p.B * p.Hkv);
-  const int slot_k = wg % nslot;
-  const int bh = wg / nslot;
-  const int hk = bh % p.Hkv;
-  const int b = bh / p.Hkv;
-  const int njobs = (p.pair_kv && 2 * slot_k + 1 != n_kt) ? 2 : 1;
-  for (int job = 0; job < njobs; ++job) {
-  if (job > 0) __syncthreads();
-  const int kt = job == 0 ? slot_k : n_kt - 1 - slot_k;
-  const int k0 = kt * C::BK;
-  const int k0w = k0 + 32 * wave;
-  const int key = k0w + l32;
-
-  const int64_t kv_slab = ((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)p.k + kv_slab, (uint32_t)(p.Nkv * C::RP));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)p.v + kv_slab, (uint32_t)(p.Nkv * C::RP));
-  u32x4 kreg[C::NC], vreg[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    kreg[c] = buf_load16(rk, (uint32_t)(key * C::RP + (2 * c + h) * 16));
-    vreg[c] = buf_load16(rv, (uint32_t)(key * C::RP + (2 * c + h) * 16));
-  }
-  f32x16 adv[C::NDB], adk[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    adv[db] = f32x16{};
-    adk[db] = f32x16{};
-    hold_acc(adv[db]);
-    hold_acc(adk[db]);
-  }
-
-  // swizzle keys: row fragments read row l32 (+ 32 qb), transposing reads
-  // rows rlo = 4h + r16/4 and rlo + 8 (+ a multiple of 16); neither offset
-  // changes a row's key
-  const int xr = rt_swz<D>(l32);
-  const int rlo = 4 * h + (r16 >> 2), rhi = rlo + 8;
-  const int xlo = rt_swz<D>(rlo), xhi = rt_swz<D>(rhi);
-  const int cpart = 2 * (g16 & 1) + ((r16 & 3) >> 1);
-  // row base and key of each read, kept as one register each
-  const int rbase = l32 * C::RP;
-  const int tbase_lo = rlo * C::RP + ((r16 & 1) << 3), tbase_hi = rhi * C::RP + ((r16 & 1) << 3);
-  auto rowfrag = [&](const char* tile, int qb, int c) {
-    const int chunk = (2 * c + h) ^ opaque_i(xr);
-    return lds_load16(tile, (uint32_t)(rbase + 32 * qb * C::RP + (chunk << 4)));
-  };
-  auto trfrag = [&](const char* tile, int r0, int db) {
-    const int chunk = 4 * db + cpart;
-    const uint32_t lo_a = (uint32_t)(tbase_lo + r0 * C::RP + ((chunk ^ opaque_i(xlo)) << 4));
-    const uint32_t hi_a = (uint32_t)(tbase_hi + r0 * C::RP + ((chunk ^ opaque_i(xhi)) << 4));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + lo_a));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + hi_a));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{l2.x, l2.y, h2.x, h2.y};
-  };
-
-  const int kv_off = p.Nkv - p.Nq;
-  const int n_qt = (p.Nq + C::BQ - 1) / C::BQ;
-  const int qt0 = p.causal ? min(max(0, k0 - kv_off) / C::BQ, n_qt) : 0;
-  const int nq = n_qt - qt0;
-  const int T = p.group * nq;
-  const float c = p.scale * kLog2e;
-
-  uint32_t voff[C::DMA];
-  dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
-  auto q_row0 = [&](int t) { return (int64_t)b * p.Hq + hk * p.group + t / nq; };
-  auto issue = [&](int t, int slot) {
-    const int q0 = (qt0 + t % nq) * C::BQ;
-    const int64_t slab = q_row0(t) * (int64_t)p.Nq * D;
-    const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
-    const i32x4 rq = sgpr_rsrc((const __bf16*)p.q + slab, (uint32_t)(p.Nq * C::RP));
-    const i32x4 ro = sgpr_rsrc((const __bf16*)p.dout + slab, (uint32_t)(p.Nq * C::RP));
-    dma_blocks<C::DMA>(rsrc_at(rq, (uint32_t)(q0 * C::RP)), dst, voff, wave);
-    dma_blocks<C::DMA>(rsrc_at(ro, (uint32_t)(q0 * C::RP)), dst + C::TILE, voff, wave);
-  };
-  float st_l = 0.0f;
-  auto load_ld = [&](int t) {
-    if (tid < 2 * C::BQ) {
-      const int r = (qt0 + t % nq) * C::BQ + (tid % C::BQ);
-      const int64_t row = q_row0(t) * (int64_t)p.Nq + r;
-      const bool live = r < p.Nq;
-      st_l = tid < C::BQ ? (live ? p.lse2[row] : INFINITY) : (live ? p.delta[row] : 0.0f);
-    }
-  };
-  auto store_ld = [&](int slot) {
-    if (tid < 2 * C::BQ) reinterpret_cast<float*>(lds + slot * C::SLOT + 2 * C::TILE)[tid] = st_l;
-  };
-
-  if (T > 0) {
-    issue(0, 0);
-    load_ld(0);
-    store_ld(0);
-  }
-  for (int t = 0; t < T; ++t) {
-    const int slot = t & 1;
-    const int q0 = (qt0 + t % nq) * C::BQ;
-    wait_vmem_all();
-    __syncthreads();  // tile t resident; the other slot (tile t-1) is free
-    if (t + 1 < T) {
-      issue(t + 1, slot ^ 1);
-      load_ld(t + 1);
-    }
-    const char* const tQ = lds + slot * C::SLOT;
-    const char* const tO = tQ + C::TILE;
-    const float* const tL = reinterpret_cast<const float*>(tQ + 2 * C::TILE);
-    const float* const tD = tL + C::BQ;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      u32x4 fq = rowfrag(tQ, qb, 0), fo = rowfrag(tO, qb, 0);
-#pragma unroll
-      for (int cc = 0; cc < C::NC; ++cc) {
-        const u32x4 cq = fq, co = fo;
-        if (cc + 1 < C::NC) {
-          fq = rowfrag(tQ, qb, cc + 1);
-          fo = rowfrag(tO, qb, cc + 1);
-        }
-        s = mfma_bf16(cq, kreg[cc], s);
-        dp = mfma_bf16(co, vreg[cc], dp);
-      }
-      // P and dS of this block (16 query rows per lane, one key per lane)
-      const int r0 = q0 + 32 * qb;
-      const bool mask = p.causal && r0 + kv_off < k0w + 31;
-      u32x4 pf[2], df[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + 32 * qb + 8 * g + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(tD + 32 * qb + 8 * g + 4 * h);
-        float e[4], d[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * g + i;
-          e[i] = exp2_fast(__builtin_fmaf(s[rr], c, -l4[i]));
-          if (mask && key > r0 + 8 * g + 4 * h + i + kv_off) e[i] = 0.0f;
-          d[i] = e[i] * (dp[rr] - d4[i]);
-        }
-        const uint32_t pe0 = pack_bf16x2(e[0], e[1]), pe1 = pack_bf16x2(e[2], e[3]);
-        const uint32_t pd0 = pack_bf16x2(d[0], d[1]), pd1 = pack_bf16x2(d[2], d[3]);
-        if (g & 1) {
-          pf[g >> 1].z = pe0; pf[g >> 1].w = pe1;
-          df[g >> 1].z = pd0; df[g >> 1].w = pd1;
-        } else {
-          pf[g >> 1].x = pe0; pf[g >> 1].y = pe1;
-          df[g >> 1].x = pd0; df[g >> 1].y = pd1;
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS over this block's two 16-row chunks
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          adv[db] = mfma_bf16(trfrag(tO, 32 * qb + 16 * kc, db), pf[kc], adv[db]);
-          adk[db] = mfma_bf16(trfrag(tQ, 32 * qb + 16 * kc, db), df[kc], adk[db]);
-          hold_acc(adv[db]);
-          hold_acc(adk[db]);
-        }
-      }
-    }
-    if (t + 1 < T) store_ld(slot ^ 1);
-  }
-
-  if (key < p.Nkv) {
-    const int64_t row = kv_slab + (int64_t)key * D;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * h;
-        store_o4(p.dv, false, row + d, adv[db][4 * g + 0], adv[db][4 * g + 1], adv[db][4 * g + 2],
-                 adv[db][4 * g + 3]);
-        store_o4(p.dk, false, row + d, adk[db][4 * g + 0] * p.scale, adk[db][4 * g + 1] * p.scale,
-                 adk[db][4 * g + 2] * p.scale, adk[db][4 * g + 3] * p.scale);
-      }
-    }
-  }
-}  // job
-}
-
 // ---- dQ -------------------------------------------------------------------------------
 
 template <int D>
@@ -629,7 +417,7 @@ struct QCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   const uint32_t lds_base =
@@ -761,17 +549,19 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void attn_bwd_dq_kernel(BwdP
   }
 }
 
-// ---- D = 512: the work of one key (or query) block split between two waves --------
+// ---- D = 256, 512: the work of one key (or query) block split between two waves ----
 // At D = 512 one wave's registers hold either the K rows or the V rows of its
 // 32 keys (128 registers each), and a dK^T or dV^T accumulator for the whole
-// head dim takes all 256 accumulation registers.  A work-group's four waves
-// therefore form two pairs over the same 32 keys.  The first wave of a pair
-// holds K, computes S = Q K^T, P = exp2(c S - lse2) (masked) and dV^T +=
-// dO^T P; the second holds V, computes dP = dO V^T, takes P from its partner
-// through LDS (float32, one barrier later), forms dS = P (dP - delta) and
-// dK^T += Q^T dS.  Each wave does the same number of products per tile (two
-// D-long contractions of a 32 x 32 block), and P is computed once.  Query
-// tiles are 32 rows (Q and dO of one tile are 64 KiB), two slots.
+// head dim takes all 256 accumulation registers; at D = 256 half of each,
+// which leaves room to read LDS fragments well ahead of the products.  A
+// work-group's four waves therefore form two pairs over the same 32 keys.
+// The first wave of a pair holds K, computes S = Q K^T, P = exp2(c S - lse2)
+// (masked) and dV^T += dO^T P; the second holds V, computes dP = dO V^T,
+// takes P from its partner through LDS (float32, one barrier later), forms
+// dS = P (dP - delta) and dK^T += Q^T dS.  Each wave does the same number of
+// products per tile (two D-long contractions of a 32 x 32 block), and P is
+// computed once.  Query tiles are 32 rows (Q and dO of one tile take 128 D
+// bytes), two slots.
 
 template <int D>
 struct KVSplitCfg {
@@ -788,6 +578,7 @@ struct KVSplitCfg {
   static constexpr int XCH = (NW / 2) * 64 * 16 * 4;   // P of each pair: 16 floats per lane
   static constexpr int LDS = 2 * SLOT + XCH;
   static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(2 * DMA <= NC, "a tile's loads fit between the first phase's products");
   static_assert(2 * BQ <= NT, "one thread per lse2 / delta value");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -873,14 +664,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
   uint32_t voff[C::DMA];
   dma_offsets_rows<C::DMA, C::RP>(voff, wave, lane, [](int row) { return rt_swz<D>(row); });
   auto q_row0 = [&](int t) { return (int64_t)b * p.Hq + hk * p.group + t / nq; };
-  auto issue = [&](int t, int slot) {
+  // descriptor of tile t of Q (or dO)
+  auto tile_rsrc = [&](int t, const void* base) {
     const int q0 = (qt0 + t % nq) * C::BQ;
     const int64_t slab = q_row0(t) * (int64_t)p.Nq * D;
+    return rsrc_at(sgpr_rsrc((const __bf16*)base + slab, (uint32_t)(p.Nq * C::RP)), (uint32_t)(q0 * C::RP));
+  };
+  auto issue = [&](int t, int slot) {
     const uint32_t dst = lds_base + (uint32_t)(slot * C::SLOT);
-    const i32x4 rq = sgpr_rsrc((const __bf16*)p.q + slab, (uint32_t)(p.Nq * C::RP));
-    const i32x4 ro = sgpr_rsrc((const __bf16*)p.dout + slab, (uint32_t)(p.Nq * C::RP));
-    dma_blocks<C::DMA>(rsrc_at(rq, (uint32_t)(q0 * C::RP)), dst, voff, wave);
-    dma_blocks<C::DMA>(rsrc_at(ro, (uint32_t)(q0 * C::RP)), dst + C::TILE, voff, wave);
+    dma_blocks<C::DMA>(tile_rsrc(t, p.q), dst, voff, wave);
+    dma_blocks<C::DMA>(tile_rsrc(t, p.dout), dst + C::TILE, voff, wave);
   };
   float st_l = 0.0f;
   auto load_ld = [&](int t) {
@@ -907,8 +700,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
     const int q0 = (qt0 + t % nq) * C::BQ;
     wait_vmem_all();
     __syncthreads();  // tile t resident; the other slot (tile t-1) and xch are free
-    if (t + 1 < T) {
-      issue(t + 1, slot ^ 1);
+    // tile t+1's loads go out one per product of the first phase below
+    const bool more = t + 1 < T;
+    const uint32_t ndst = lds_base + (uint32_t)((slot ^ 1) * C::SLOT);
+    i32x4 nrq = {}, nro = {};
+    if (more) {
+      nrq = tile_rsrc(t + 1, p.q);
+      nro = tile_rsrc(t + 1, p.dout);
       load_ld(t + 1);
     }
     const char* const tQ = lds + slot * C::SLOT;
@@ -935,6 +733,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
       constexpr int cc = decltype(cI)::value;
       __builtin_amdgcn_sched_barrier(0);
       x = mfma_bf16(f[cc % W], reg[cc], x);
+      if constexpr (cc < 2 * C::DMA) {
+        if (more) {
+          if constexpr (cc % 2 == 0) dma_block_one<C::DMA>(nrq, ndst, voff, wave, cc / 2);
+          else dma_block_one<C::DMA>(nro, ndst + C::TILE, voff, wave, cc / 2);
+        }
+      }
       if constexpr (cc + W < C::NC) f[cc % W] = rowfrag(tR, cc + W);
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -1013,12 +817,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
 }  // job
 }
 
-// dQ at D = 512: pairs of waves over the same 32 query rows.  The first wave
-// holds the Q rows and computes S^T = K Q^T and P^T, the second holds the dO
-// rows and computes dP^T = V dO^T; they swap the two through LDS (float32),
-// both form dS^T = P^T (dP^T - delta) from the same values, and each
-// accumulates one half of dQ^T += K^T dS^T (d below or above D / 2).  Key
-// tiles are 32 keys (K and V of one tile are 64 KiB), two slots.
+// dQ at D = 256 and 512: pairs of waves over the same 32 query rows.  The
+// first wave holds the Q rows and computes S^T = K Q^T and P^T, the second
+// holds the dO rows and computes dP^T = V dO^T; they swap the two through LDS
+// (float32), both form dS^T = P^T (dP^T - delta) from the same values, and
+// each accumulates one half of dQ^T += K^T dS^T (d below or above D / 2).
+// Key tiles are 32 keys (K and V of one tile take 128 D bytes), two slots.
 
 template <int D>
 struct QSplitCfg {
@@ -1036,6 +840,7 @@ struct QSplitCfg {
   static constexpr int XCH = NW * 64 * 16 * 4;   // each wave's S or dP block
   static constexpr int LDS = 2 * SLOT + XCH;
   static_assert(TILE % (1024 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(2 * DMA <= NC, "a tile's loads fit between the first phase's products");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -1136,11 +941,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
     const int slot = kt & 1;
     wait_vmem_all();
     __syncthreads();  // tile kt resident; the other slot and the exchange are free
-    if (kt + 1 < n_kt) issue(kt + 1, slot ^ 1);
     const int key0 = kt * C::BC;
     // uniform over the pair: its rows see none of the tile (the barriers
     // below are still taken)
     const bool skip = p.causal && key0 > q0w + 31 + kv_off;
+    // tile kt+1's loads: one per product of the first phase below (all at
+    // once here when this wave skips the tile)
+    const bool more = kt + 1 < n_kt;
+    const uint32_t ndst = lds_base + (uint32_t)((slot ^ 1) * C::SLOT);
+    const i32x4 nrk = rsrc_at(rk, (uint32_t)((kt + 1) * C::TILE));
+    const i32x4 nrv = rsrc_at(rv, (uint32_t)((kt + 1) * C::TILE));
+    if (more && skip) issue(kt + 1, slot ^ 1);
     const char* const tK = lds + slot * C::SLOT;
     const char* const tV = tK + C::TILE;
     const bool mask = key0 + C::BC > p.Nkv || (p.causal && key0 + C::BC - 1 > q0w + kv_off);
@@ -1161,6 +972,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
         constexpr int cc = decltype(cI)::value;
         __builtin_amdgcn_sched_barrier(0);
         x = mfma_bf16(f[cc % W], reg[cc], x);
+        if constexpr (cc < 2 * C::DMA) {
+          if (more) {
+            if constexpr (cc % 2 == 0) dma_block_one<C::DMA>(nrk, ndst, voff, wave, cc / 2);
+            else dma_block_one<C::DMA>(nrv, ndst + C::TILE, voff, wave, cc / 2);
+          }
+        }
         if constexpr (cc + W < C::NC) f[cc % W] = rowfrag(tR, cc + W);
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -1238,8 +1055,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
 
 template <int D>
 hipError_t launch(const BwdParams& p0, hipStream_t stream) {
-  // D = 512 runs the kernels that split each block between two waves
-  constexpr bool split = D > 256;
+  // D = 256 and 512 run the kernels that split each block between two waves
+  constexpr bool split = D > 128;
   constexpr int BK = split ? KVSplitCfg<D>::BK : KVCfg<D>::BK;
   constexpr int BR = split ? QSplitCfg<D>::BR : QCfg<D>::BR;
   BwdParams p = p0;
@@ -1257,10 +1074,8 @@ hipError_t launch(const BwdParams& p0, hipStream_t stream) {
   if (err != hipSuccess) return err;
   if constexpr (split)
     hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<D>), dim3((unsigned)kv_wg), dim3(KVSplitCfg<D>::NT), 0, stream, p);
-  else if constexpr (D <= 128)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_bwd_dkdv_wide_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)kv_wg), dim3(KVCfg<D>::NT), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (split)

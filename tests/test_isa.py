@@ -34,13 +34,9 @@ KNOWN_SCRATCH = {
     # (168 of 170 VGPRs): stored before the loop, reloaded after it
     ("attn_fwd_bf16.hip", "attn_fwd_bf16_kernelILi128ELi32E"): 12,
     ("attn_fwd_wide.hip", "attn_fwd_wide_kernelILi512E"): 24,
-    # backward at D = 256, one wave per SIMD with all 512 registers taken:
-    # dK/dV stores before and reloads after each query-tile loop; dQ also
-    # reloads two Q fragments per key tile
-    ("attn_bwd.hip", "attn_bwd_dkdv_wide_kernelILi256E"): 208,
-    ("attn_bwd.hip", "attn_bwd_dq_kernelILi256E"): 108,
-    # D = 512 dK/dV: the same, before and after each query-tile loop, plus one
-    # dword reloaded per tile
+    # backward dK/dV at D = 512, one wave per SIMD with all 512 registers
+    # taken: values stored before and reloaded after each query-tile loop,
+    # plus one dword reloaded per tile
     ("attn_bwd.hip", "attn_bwd_dkdv_split_kernelILi512E"): 204,
 }
 
