@@ -278,6 +278,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       to[w] = trf(tO, r0, j % C::NDB);
       tq[w] = trf(tQ, r0, j % C::NDB);
     };
+    // lse2 and delta of block qb's 16 rows per lane.  The causal mask goes
+    // into lse2: a row that must not see this lane's key gets +inf, so its P
+    // is exp2(-inf) = 0; only blocks that cross the wave's keys pay for it.
     auto load_ld_block = [&](int qb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -286,17 +289,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         L[4 * j + 0] = l4.x; L[4 * j + 1] = l4.y; L[4 * j + 2] = l4.z; L[4 * j + 3] = l4.w;
         Dl[4 * j + 0] = d4.x; Dl[4 * j + 1] = d4.y; Dl[4 * j + 2] = d4.z; Dl[4 * j + 3] = d4.w;
       }
+      const int r0 = q0 + 32 * qb;
+      if (p.causal && r0 + kv_off < k0w + 31) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if (key > r0 + 8 * (rr / 4) + 4 * h + (rr % 4) + kv_off) L[rr] = INFINITY;
+      }
     };
     // softmax and dS of elements r .. r+1 (a packed pair) of block qb
     auto soft2 = [&](int qb, int r, const f32x16& sv, const f32x16& dv) {
-      const int r0 = q0 + 32 * qb;
-      const bool mask = p.causal && r0 + kv_off < k0w + 31;
       float e[2], d[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int rr = r + i;
         e[i] = exp2_fast(__builtin_fmaf(sv[rr], c, -L[rr]));
-        if (mask && key > r0 + 8 * (rr / 4) + 4 * h + (rr % 4) + kv_off) e[i] = 0.0f;
         d[i] = e[i] * (dv[rr] - Dl[rr]);
       }
       const uint32_t pe = pack_bf16x2(e[0], e[1]), pd = pack_bf16x2(d[0], d[1]);
@@ -514,10 +520,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       }
       float dsv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = exp2_fast(__builtin_fmaf(s[r], c, -lq));
-        if (mask && key0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
-        dsv[r] = e * (dp[r] - dq_row);
+      for (int r = 0; r < 16; ++r) dsv[r] = exp2_fast(__builtin_fmaf(s[r], c, -lq)) * (dp[r] - dq_row);
+      // keys past the end or after the row (tail and causal-diagonal tiles
+      // only: the compare and select are skipped elsewhere)
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4) > klim) dsv[r] = 0.0f;
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -750,19 +759,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
     });
     float pv[16];  // P (role 0)
     if (role == 0) {
-      const bool mask = p.causal && q0 + kv_off < k0w + 31;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + 8 * g + 4 * h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e = exp2_fast(__builtin_fmaf(x[4 * g + i], c, -l4[i]));
-          if (mask && key > q0 + 8 * g + 4 * h + i + kv_off) e = 0.0f;
-          pv[4 * g + i] = e;
-        }
+        for (int i = 0; i < 4; ++i) pv[4 * g + i] = exp2_fast(__builtin_fmaf(x[4 * g + i], c, -l4[i]));
+      }
+      // rows before this lane's key (only tiles that cross the pair's keys)
+      if (p.causal && q0 + kv_off < k0w + 31) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key > q0 + 8 * (r / 4) + 4 * h + (r % 4) + kv_off) pv[r] = 0.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4*>(xch + 4 * (64 * g + lane)) =
             f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
-      }
     }
     __syncthreads();  // P of the pair visible to its second wave
     u32x4 fr[2];
@@ -989,10 +1001,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
       // role 0: P; role 1: dP as it stands
       if (role == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = exp2_fast(__builtin_fmaf(x[r], c, -lq));
-          if (mask && key0 + 8 * (r / 4) + 4 * h + (r % 4) > klim) e = 0.0f;
-          xv[r] = e;
+        for (int r = 0; r < 16; ++r) xv[r] = exp2_fast(__builtin_fmaf(x[r], c, -lq));
+        // keys past the end or after the row (tail and diagonal tiles only)
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key0 + 8 * (r / 4) + 4 * h + (r % 4) > klim) xv[r] = 0.0f;
         }
       } else {
 #pragma unroll
