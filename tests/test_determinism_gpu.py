@@ -4,13 +4,15 @@ contribution": outputs identical in every launch).
 
 No kernel here uses atomics or a reduction whose order depends on timing,
 so two launches on the same inputs must agree bit for bit, O and LSE.  Each
-case runs the configuration the dispatcher picks for its shape: the
-direct-to-LDS kernel with 64-key tiles (small grids) and with 32-key tiles
-at three waves per SIMD (grids of at least three work-groups per compute
-unit), with and without causal tile pairing; the wide-head kernel (64- and
-32-key tiles); the split-D kernel; the generic tiled kernel; the e4m3 path
-with per-tensor and with block descales; the e4m3-probability kernel, exact
-and Lean P codes.
+case runs the configuration the dispatcher picks for its shape: the bf16
+kernel of head dims 64 and 128 with 64-key tiles (small grids) and with
+32-key tiles at three waves per SIMD (grids of at least three work-groups
+per compute unit), with and without causal tile pairing; the wide-head
+kernel (64- and 32-key tiles); the four-wave split-D kernel (D = 768, and an
+odd multiple of 32 on its padded layout) and the eight-wave one (D = 1024);
+the generic tiled kernel; the e4m3 path with per-tensor and with block
+descales; the e4m3-probability kernel, exact and Lean P codes.  The
+backward's determinism is tested with its parity tests.
 """
 import sys
 
@@ -51,8 +53,9 @@ BF16 = [
     (1, 8, 8, 1000, 1000, 64, True),     # direct-to-LDS, D = 64
     (1, 4, 2, 600, 777, 320, True),      # wide-head kernel, 64-key tiles
     (1, 4, 2, 600, 777, 512, False),     # wide-head kernel, 32-key tiles
-    (1, 4, 4, 500, 650, 768, False),     # split-D
-    (1, 4, 2, 500, 650, 1024, True),     # split-D
+    (1, 4, 4, 500, 650, 768, False),     # split-D, four waves
+    (1, 4, 2, 300, 411, 416, True),      # split-D, four waves, D + 32 layout
+    (1, 4, 2, 500, 650, 1024, True),     # split-D, eight waves
     (1, 4, 2, 300, 411, 96, True),       # generic tiled kernel
 ]
 
