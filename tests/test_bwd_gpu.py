@@ -132,14 +132,15 @@ def test_bwd_deterministic(D):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_bwd_scale_variants():
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_bwd_scale_variants(D):
     """Scale 0 (uniform P: dQ = dK = 0) and a negative scale."""
-    w = Workload("bwd_sc", 1, 2, 2, 150, 170, 64, True, "bf16", seed=7)
+    w = Workload("bwd_sc", 1, 2, 2, 150, 170, D, True, "bf16", seed=7)
     q, k, v = make_inputs(w)
     g = make_grad(w)
     dev = [t.cuda() for t in (q, k, v, g)]
     for sc in (0.0, -0.11):
-        note(f"bwd scale={sc}")
+        note(f"bwd D={D} scale={sc}")
         O, L = A.fwd(dev[0], dev[1], dev[2], causal=True, scale=sc)
         dq, dk, dv = A.bwd(dev[0], dev[1], dev[2], O, L, dev[3], causal=True, scale=sc)
         torch.cuda.synchronize()
