@@ -153,31 +153,41 @@ def test_bwd_scale_variants(D):
                 assert rel_err(x, r) <= TOL, (sc, name, rel_err(x, r))
 
 
-# (Hq, D); B = 1, N = 4096, causal
-FULL_SIZE = {"causal_d256": (8, 256)}
+# (Hq, Hkv, D); B = 1, N = 4096, causal
+FULL_SIZE = {"causal_d256": (8, 8, 256), "gqa_causal_d512": (32, 8, 512)}
 
 
 # bwd_causal_bf16_d512: 32 heads are enough work for the dK/dV launch to
 # pair its causal key tiles
-@pytest.mark.parametrize("name", ["prefill_causal_bf16", "causal_d256", "bwd_causal_bf16_d512"])
+@pytest.mark.parametrize("name", ["prefill_causal_bf16", "causal_d256", "bwd_causal_bf16_d512", "gqa_causal_d512"])
 def test_bwd_full_size_sampled(name):
-    """The benchmarked problem (B4 H32 N4096 D128, causal), B1 H8 N4096 D256
-    and B1 H32 N4096 D512 (causal): every gradient of three sampled heads
-    against the oracle's per-head gradients."""
+    """The benchmarked problem (B4 H32 N4096 D128, causal), B1 H8 N4096 D256,
+    B1 H32 N4096 D512 and its GQA form with 8 KV heads (causal): for three
+    sampled KV heads, dQ of every query head of the group against the
+    oracle's per-head gradients, and dK, dV against their sums over the
+    group."""
     if name in WORKLOADS:
         w = WORKLOADS[name]
     else:
-        H, D = FULL_SIZE[name]
-        w = Workload(name, 1, H, H, 4096, 4096, D, True, "bf16")
+        Hq, Hkv, D = FULL_SIZE[name]
+        w = Workload(name, 1, Hq, Hkv, 4096, 4096, D, True, "bf16")
     note(f"{w.name} backward, full size")
     (q, k, v, g), (dq, dk, dv) = run_bwd(w)
     rng = np.random.default_rng(2)
-    heads = [(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))]
+    G = w.Hq // w.Hkv
+    # three KV heads; every query head of each one's group
+    kv_heads = [(0, 0), (w.B - 1, w.Hkv - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hkv)))]
     worst = 0.0
-    for b, h in heads:
-        r_q, r_k, r_v = oracle.attention_backward_head(
-            *(t[b, h].to(torch.float64).numpy() for t in (q, k, v, g)), scale=w.scale, causal=w.causal)
-        for x, r in ((dq[b, h], r_q), (dk[b, h], r_k), (dv[b, h], r_v)):
-            worst = max(worst, rel_err(x, r))
-    note(f"{w.name}: worst max |err| / max |ref| over 3 heads = {worst:.3e}")
+    for b, hk in kv_heads:
+        kh, vh = (t[b, hk].to(torch.float64).numpy() for t in (k, v))
+        sum_k = sum_v = 0.0
+        for hq in range(hk * G, (hk + 1) * G):
+            r_q, r_k, r_v = oracle.attention_backward_head(q[b, hq].to(torch.float64).numpy(), kh, vh,
+                                                           g[b, hq].to(torch.float64).numpy(), scale=w.scale,
+                                                           causal=w.causal)
+            worst = max(worst, rel_err(dq[b, hq], r_q))
+            sum_k = sum_k + r_k
+            sum_v = sum_v + r_v
+        worst = max(worst, rel_err(dk[b, hk], sum_k), rel_err(dv[b, hk], sum_v))
+    note(f"{w.name}: worst max |err| / max |ref| over 3 KV heads = {worst:.3e}")
     assert worst <= TOL
