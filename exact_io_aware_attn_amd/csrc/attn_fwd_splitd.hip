@@ -48,6 +48,10 @@ namespace attn {
 
 namespace {
 
+// An empty asm that takes x and gives it back in the same vector register:
+// the computation of x cannot be moved past it.
+__device__ __forceinline__ void pin_f(float& x) { asm volatile("" : "+v"(x)); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;
@@ -294,20 +298,25 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
       m_run = m_new;
     }
     const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
+    // P of keys 0..15 now; that of keys 16..31 between the first half of the
+    // P V MFMAs below, which use only the first (spread evenly over them and
+    // pinned there: left to the compiler they are moved past every MFMA to
+    // their first use)
     u32x4 pf[2];
-    float ls = l_run;
+    float e[16];
+    auto expo = [&](int i) {
+      e[i] = exp2_fast(s[i] + mneg);
+      pin_f(e[i]);
+    };
+    auto pack = [&](int s16) {
+      pf[s16].x = pack_bf16x2(e[8 * s16 + 0], e[8 * s16 + 1]);
+      pf[s16].y = pack_bf16x2(e[8 * s16 + 2], e[8 * s16 + 3]);
+      pf[s16].z = pack_bf16x2(e[8 * s16 + 4], e[8 * s16 + 5]);
+      pf[s16].w = pack_bf16x2(e[8 * s16 + 6], e[8 * s16 + 7]);
+    };
 #pragma unroll
-    for (int s16 = 0; s16 < 2; ++s16) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = exp2_fast(s[8 * s16 + i] + mneg);
-      pf[s16].x = pack_bf16x2(e[0], e[1]);
-      pf[s16].y = pack_bf16x2(e[2], e[3]);
-      pf[s16].z = pack_bf16x2(e[4], e[5]);
-      pf[s16].w = pack_bf16x2(e[6], e[7]);
-      ls += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    }
-    l_run = ls;
+    for (int i = 0; i < 8; ++i) expo(i);
+    pack(0);
 
     // ---- O^T[D/2 rows] += V^T P^T ------------------------------------------------------
     // V fragments (two transposing reads each) through a rolling window of
@@ -329,14 +338,26 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_splitd_kernel(FwdParams p) {
       for (int f = 0; f < NF; ++f) {
         const u32x4 cur = vf[f % C::LV];
         if (f + C::LV < NF) vf[f % C::LV] = vfrag(f + C::LV);
+        if (f == C::NDB) pack(1);
         __builtin_amdgcn_sched_barrier(0);
         acc[f % C::NDB] = mfma_bf16(cur, pf[f / C::NDB], acc[f % C::NDB]);
+        if (f < C::NDB) {
+#pragma unroll
+          for (int i = (8 * f + C::NDB - 1) / C::NDB; i < (8 * (f + 1) + C::NDB - 1) / C::NDB; ++i) expo(8 + i);
+        }
         if (k_next) {
           // blocks KS .. DMA_WAVE - 1, one after each of the first MFMAs
           if (C::KS + f < C::DMA_WAVE) dma_block_at<C::DMA_WAVE>(rk_n, lk, dma_off(false, C::KS + f), wave, C::KS + f);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    {
+      float ls = l_run;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        ls += ((e[4 * g + 0] + e[4 * g + 1]) + (e[4 * g + 2] + e[4 * g + 3]));
+      l_run = ls;
     }
     wait_vmem_all();   // K(kt+1) resident
     __syncthreads();   // V buffer free, exchange area read, K(kt+1) visible

@@ -45,6 +45,12 @@ namespace attn {
 
 namespace {
 
+// An empty asm that takes x and gives it back in the same vector register:
+// computed values cannot be moved past it.  Without it the exponentials of
+// P_t, which are only used after the loop over the P V MFMAs, are sunk
+// below all of them and no longer overlap the matrix work.
+__device__ __forceinline__ void pin_f(float& x) { asm volatile("" : "+v"(x)); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
@@ -255,7 +261,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
     float e[C::NE];
     auto exps = [&](int lo, int hi) {
 #pragma unroll
-      for (int i = lo; i < hi; ++i) e[i] = exp2_fast(__builtin_fmaf(s[i / 16][i % 16], c, mneg));
+      for (int i = lo; i < hi; ++i) {
+        e[i] = exp2_fast(__builtin_fmaf(s[i / 16][i % 16], c, mneg));
+        pin_f(e[i]);
+      }
     };
     if constexpr (PV) {
       const bool v_now = t < n_kt;  // V_t streams in meanwhile
