@@ -78,6 +78,8 @@ _P8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_p8.hip")
 # the split-D kernels: four waves (D up to 960) and eight (D = 1024)
 _SPLITD = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_splitd.hip")
 _SPLITD8 = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_splitd8.hip")
+# the wide-head kernel (bf16 D = 192..512)
+_WIDE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_wide.hip")
 # the backward's three launches
 _BWD = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.h", "attn_bwd.hip")
 MEASURED_TRAFFIC = {
@@ -90,9 +92,8 @@ MEASURED_TRAFFIC = {
     # write each byte once)
     "fp8_blocks_outlier": (_PIPE, "b950ecf36dbe34db", 188260.78125 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (_SPLITD8, "dca91d739d485894", 163938.5 * 2 * 1024, 68142.9375 * 1024),
-    "splitd_bf16_d768": (_SPLITD, "c9934ca1a03d742f", 123049.5 * 2 * 1024, 49280.0 * 1024),
-    "splitd_bf16_d512": (("attn_common.h", "attn_dma.h", "attn_fwd_wide.hip"), "5953b003aef0a2d8",
-                         49596.0 * 2 * 1024, 33408.0 * 1024),
+    "splitd_bf16_d768": (_SPLITD, "5de55f883bc0be40", 123050.0 * 2 * 1024, 49280.0 * 1024),
+    "splitd_bf16_d512": (_WIDE, "5a59529a30cce99e", 49596.0 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
     "chunk_prefill_splitkv_bf16": (_BF16, "53fd85dcaa8ecb48", 73817.6875 * 2 * 1024, 33024.0 * 1024),
