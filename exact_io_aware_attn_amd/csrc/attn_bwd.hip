@@ -77,6 +77,10 @@ __device__ __forceinline__ void hold_acc(f32x16& x) { asm volatile("" : "+a"(x))
 // (the MFMA reads its A/B operands from accumulation registers as well).
 __device__ __forceinline__ void hold_frag(u32x4& x) { asm volatile("" : "+a"(x)); }
 
+// An empty asm that takes x and gives it back in the same vector register:
+// the computation of x cannot be moved past it.
+__device__ __forceinline__ void pin_u(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -305,7 +309,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         e[i] = exp2_fast(__builtin_fmaf(sv[rr], c, -L[rr]));
         d[i] = e[i] * (dv[rr] - Dl[rr]);
       }
-      const uint32_t pe = pack_bf16x2(e[0], e[1]), pd = pack_bf16x2(d[0], d[1]);
+      uint32_t pe = pack_bf16x2(e[0], e[1]), pd = pack_bf16x2(d[0], d[1]);
+      // kept in this step: used only by the next phase's MFMAs, they would
+      // otherwise be moved past all of this phase's
+      pin_u(pe);
+      pin_u(pd);
       const int kc = r / 8, comp = (r % 8) / 2;
       if (comp == 0) { pf[qb][kc].x = pe; df[qb][kc].x = pd; }
       else if (comp == 1) { pf[qb][kc].y = pe; df[qb][kc].y = pd; }
