@@ -98,9 +98,9 @@ MEASURED_TRAFFIC = {
     # it reads and writes its parts once)
     "chunk_prefill_splitkv_bf16": (_BF16, "53fd85dcaa8ecb48", 73817.6875 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
-    "bwd_causal_bf16": (_BWD, "6feef2939a2b0ba8", 677313.875 * 2 * 1024, 397631.625 * 1024),
-    "bwd_causal_bf16_d256": (_BWD, "6feef2939a2b0ba8", 693414.0 * 2 * 1024, 396433.84375 * 1024),
-    "bwd_causal_bf16_d512": (_BWD, "6feef2939a2b0ba8", 998783.65625 * 2 * 1024, 446722.28125 * 1024),
+    "bwd_causal_bf16": (_BWD, "aea0e4d8aaaa2175", 676829.3125 * 2 * 1024, 397319.8125 * 1024),
+    "bwd_causal_bf16_d256": (_BWD, "aea0e4d8aaaa2175", 690384.0625 * 2 * 1024, 395630.90625 * 1024),
+    "bwd_causal_bf16_d512": (_BWD, "aea0e4d8aaaa2175", 1013150.34375 * 2 * 1024, 446470.296875 * 1024),
     "prefill_causal_bf16_poly": (_PIPE, "b950ecf36dbe34db", 266960.84375 * 2 * 1024, 133123.546875 * 1024),
     "fp8_p8_outlier": (_P8, "40c93540ee3a0f74", 169015.1875 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_outlier": (_P8, "40c93540ee3a0f74", 122964.25 * 2 * 1024, 99840.0 * 1024),
