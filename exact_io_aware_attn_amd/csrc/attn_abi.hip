@@ -390,8 +390,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                 need);
   if (dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "the backward pass takes bf16 only (dtype=%d)", dtype);
-  if (D != 64 && D != 128 && D != 256 && D != 512)
-    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the backward pass takes D = 64, 128, 256 or 512",
+  if (D % 64 != 0 || D < 64 || D > 512)
+    return fail(ATTN_ERR_UNSUPPORTED, "D=%lld unsupported: the backward pass takes D a multiple of 64 up to 512",
                 (long long)D);
   const int64_t lim = (int64_t)1 << 31;
   if (Nq * D * 2 >= lim || Nkv * D * 2 >= lim)

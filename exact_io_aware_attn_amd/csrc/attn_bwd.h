@@ -6,7 +6,7 @@
 
 namespace attn {
 
-// Backward pass (bf16, D = 64, 128, 256 or 512): dQ, dK, dV from Q, K, V, the forward
+// Backward pass (bf16, D a multiple of 64 up to 512): dQ, dK, dV from Q, K, V, the forward
 // O and LSE and the upstream dO.  delta and lse2 are (B, Hq, Nq) float32
 // workspace arrays the first launch fills.
 struct BwdParams {

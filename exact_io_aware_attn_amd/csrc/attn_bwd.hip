@@ -1,5 +1,5 @@
-// attn_bwd.hip -- exact attention backward on gfx950 (bf16, D = 64, 128, 256
-// and 512).
+// attn_bwd.hip -- exact attention backward on gfx950 (bf16, D = 64 and 128,
+// and every multiple of 64 from 192 to 512).
 //
 // FlashAttention summary page, method paragraph: the backward pass recomputes
 // S = Q K^T instead of storing it; FlashAttention v1/v2/v3/v4 blog post,
@@ -32,8 +32,8 @@
 //
 // D = 64 and 128: one wave holds both K and V of its keys (dK/dV, 128 keys
 // and one wave per SIMD per work-group, 64-row Q/dO tiles) or both Q and dO
-// of its rows (dQ, 128 rows, two waves per SIMD, 64-key K/V tiles).  D = 256
-// and 512: those registers no longer fit, and the work of each block is
+// of its rows (dQ, 128 rows, two waves per SIMD, 64-key K/V tiles).  D = 192
+// to 512: those registers no longer fit, and the work of each block is
 // split between the two waves of a pair (the split kernels below).
 //
 // Q/dO and K/V tiles stream into LDS with direct-to-LDS buffer loads, two
@@ -86,15 +86,24 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(f
 
 // ---- prep: delta = rowsum(dO * O), lse2 = LSE log2(e) ---------------------------------
 
+// lanes per row of the prep kernel: 16 bytes each, rounded up to a power of
+// two so that the shuffle reduction stays within a row
+template <int D>
+constexpr int prep_lanes() {
+  int n = 1;
+  while (n < D / 8) n *= 2;
+  return n;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;       // lanes per row, 16 bytes each
+  constexpr int LPR = prep_lanes<D>();
   constexpr int RPB = 256 / LPR;   // rows per work-group
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
   float acc = 0.0f;
-  if (row < rows) {
+  if (row < rows && sub < D / 8) {
     const u32x4 a = *reinterpret_cast<const u32x4*>((const __bf16*)p.o + row * D + sub * 8);
     const u32x4 g = *reinterpret_cast<const u32x4*>((const __bf16*)p.dout + row * D + sub * 8);
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// ---- D = 256, 512: the work of one key (or query) block split between two waves ----
+// ---- D = 192 .. 512: the work of one key (or query) block split between two waves ---
 // At D = 512 one wave's registers hold either the K rows or the V rows of its
 // 32 keys (128 registers each), and a dK^T or dV^T accumulator for the whole
 // head dim takes all 256 accumulation registers; at D = 256 half of each,
@@ -837,7 +846,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_split_kernel(BwdParams p
 }  // job
 }
 
-// dQ at D = 256 and 512: pairs of waves over the same 32 query rows.  The
+// dQ at D = 192 .. 512: pairs of waves over the same 32 query rows.  The
 // first wave holds the Q rows and computes S^T = K Q^T and P^T, the second
 // holds the dO rows and computes dP^T = V dO^T; they swap the two through LDS
 // (float32), both form dS^T = P^T (dP^T - delta) from the same values, and
@@ -1077,13 +1086,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_split_kernel(BwdParams p) 
 
 template <int D>
 hipError_t launch(const BwdParams& p0, hipStream_t stream) {
-  // D = 256 and 512 run the kernels that split each block between two waves
+  // D from 192 run the kernels that split each block between two waves
   constexpr bool split = D > 128;
   constexpr int BK = split ? KVSplitCfg<D>::BK : KVCfg<D>::BK;
   constexpr int BR = split ? QSplitCfg<D>::BR : QCfg<D>::BR;
   BwdParams p = p0;
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-  const int64_t prep_wg = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+  constexpr int RPB = 256 / prep_lanes<D>();
+  const int64_t prep_wg = (rows + RPB - 1) / RPB;
   const int n_kt = (p.Nkv + BK - 1) / BK;
   const int n_qt = (p.Nq + BR - 1) / BR;
   p.pair_kv = pair_causal_grid(p.causal, (int64_t)p.B * p.Hkv, n_kt, p.Nq, p.Nkv);
@@ -1113,7 +1123,11 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   switch (p.D) {
     case 64: return launch<64>(p, stream);
     case 128: return launch<128>(p, stream);
+    case 192: return launch<192>(p, stream);
     case 256: return launch<256>(p, stream);
+    case 320: return launch<320>(p, stream);
+    case 384: return launch<384>(p, stream);
+    case 448: return launch<448>(p, stream);
     case 512: return launch<512>(p, stream);
     default: return hipErrorInvalidValue;
   }

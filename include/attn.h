@@ -330,7 +330,7 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq);
  *   o, lse         : the forward outputs for the same q, k, v, causal, scale
  *   workspace      : DEVICE, 16-byte aligned, >= attn_bwd_workspace_bytes;
  *                    overwritten (the library allocates nothing)
- *   dtype          : ATTN_BF16 only; D = 64, 128, 256 or 512; causal and scale as
+ *   dtype          : ATTN_BF16 only; D a multiple of 64 up to 512; causal and scale as
  *                    attn_fwd (any finite scale).
  * Outputs are overwritten (not accumulated into).  float32 accumulation;
  * every output element is accumulated by one wave, without atomics, so

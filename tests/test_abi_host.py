@@ -221,7 +221,7 @@ def test_bwd_invalid_arguments(kw):
     assert bwd_call(**kw) == A.ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(D=96), dict(D=384), dict(D=1024), dict(dtype=A.ATTN_F32), dict(dtype=A.ATTN_FP8_E4M3)])
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=160), dict(D=576), dict(D=1024), dict(dtype=A.ATTN_F32), dict(dtype=A.ATTN_FP8_E4M3)])
 def test_bwd_unsupported(kw):
     assert bwd_call(**kw) == A.ATTN_ERR_UNSUPPORTED
 

@@ -88,6 +88,13 @@ CASES = [
     (1, 2, 2, 300, 1, 512, True),         # one key
     (1, 3, 1, 97, 97, 512, True),         # MQA, one query tile of each pair ragged
     (1, 2, 2, 256, 256, 512, True),       # whole tiles on the diagonal
+    # the other multiples of 64 on the split kernels (rows of 24, 40, 48 and
+    # 56 16-byte chunks; the prep kernel with idle lanes)
+    (1, 2, 2, 200, 300, 192, True),
+    (2, 4, 2, 130, 257, 320, False),
+    (1, 2, 1, 333, 129, 384, True),
+    (1, 3, 1, 97, 97, 448, True),
+    (1, 2, 2, 1, 70, 384, True),
 ]
 
 

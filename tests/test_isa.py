@@ -38,6 +38,7 @@ KNOWN_SCRATCH = {
     # taken: values stored before and reloaded after each query-tile loop,
     # plus one dword reloaded per tile
     ("attn_bwd.hip", "attn_bwd_dkdv_split_kernelILi512E"): 204,
+    ("attn_bwd.hip", "attn_bwd_dkdv_split_kernelILi448E"): 96,
 }
 
 SCALAR_WRITE = re.compile(r"\bs_(store|buffer_store|scratch_store|dcache_wb|dcache_discard|atomic|buffer_atomic)")
