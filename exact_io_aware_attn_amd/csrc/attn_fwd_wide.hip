@@ -196,6 +196,17 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
     const char* const kb_cur = lds + (t & 1) * C::TILE;
     const char* const vb_prev = ldsV + ((t - 1) & 1) * C::TILE;
 
+    // V_{t-1} fragment f (two transposing reads)
+    auto vfrag = [&](int f) {
+      const int s16 = f / C::NDB, db = f % C::NDB;
+      const uint32_t a0 = voff(db) + (uint32_t)(s16 * 16 * C::RP);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_prev + a0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_prev + a0 + 8 * C::RP));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2.x, l2.y, h2.x, h2.y};
+    };
+    u32x4 vf[C::LV];
+
     // ---- S_t^T = K_t Q^T, K_{t+1} streaming in between the MFMAs --------------
     f32x16 s[NKB];
 #pragma unroll
@@ -218,6 +229,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
         // one load block after each of the first MFMAs: the tile lands well
         // before the barrier that needs it
         if (k_next && f < C::DMA_WAVE) dma_block_at<C::DMA_WAVE>(rk_n, k_slot(t + 1), dma_off(false, f), wave, f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the first V fragments of the P V product below, read while the
+      // MFMAs drain and the row maximum is formed
+      if constexpr (PV) {
+#pragma unroll
+        for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(i);
         __builtin_amdgcn_sched_barrier(0);
       }
       // mask (tiles crossing the diagonal or the key tail only)
@@ -269,17 +287,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_wide_kernel(FwdParams p) {
     if constexpr (PV) {
       const bool v_now = t < n_kt;  // V_t streams in meanwhile
       const i32x4 rv_t = rsrc_at(rv, (uint32_t)(t * C::TILE));
-      auto vfrag = [&](int f) {
-        const int s16 = f / C::NDB, db = f % C::NDB;
-        const uint32_t a0 = voff(db) + (uint32_t)(s16 * 16 * C::RP);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_prev + a0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb_prev + a0 + 8 * C::RP));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2.x, l2.y, h2.x, h2.y};
-      };
-      u32x4 vf[C::LV];
+      if constexpr (!QK) {
 #pragma unroll
-      for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(i);
+        for (int i = 0; i < C::LV; ++i) vf[i] = vfrag(i);
+      }
 #pragma unroll
       for (int f = 0; f < C::NFV; ++f) {
         const u32x4 cur = vf[f % C::LV];
