@@ -93,14 +93,14 @@ MEASURED_TRAFFIC = {
     "fp8_blocks_outlier": (_PIPE, "b950ecf36dbe34db", 188260.78125 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (_SPLITD8, "dca91d739d485894", 163938.5 * 2 * 1024, 68142.9375 * 1024),
     "splitd_bf16_d768": (_SPLITD, "5de55f883bc0be40", 123050.0 * 2 * 1024, 49280.0 * 1024),
-    "splitd_bf16_d512": (_WIDE, "5a59529a30cce99e", 49596.0 * 2 * 1024, 33408.0 * 1024),
+    "splitd_bf16_d512": (_WIDE, "f6d4df4d3cdd1c55", 49594.5 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
     "chunk_prefill_splitkv_bf16": (_BF16, "53fd85dcaa8ecb48", 73817.6875 * 2 * 1024, 33024.0 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
-    "bwd_causal_bf16": (_BWD, "aea0e4d8aaaa2175", 676829.3125 * 2 * 1024, 397319.8125 * 1024),
-    "bwd_causal_bf16_d256": (_BWD, "aea0e4d8aaaa2175", 690384.0625 * 2 * 1024, 395630.90625 * 1024),
-    "bwd_causal_bf16_d512": (_BWD, "aea0e4d8aaaa2175", 1013150.34375 * 2 * 1024, 446470.296875 * 1024),
+    "bwd_causal_bf16": (_BWD, "6e982fcd75cec507", 678817.5 * 2 * 1024, 397390.265625 * 1024),
+    "bwd_causal_bf16_d256": (_BWD, "6e982fcd75cec507", 692962.03125 * 2 * 1024, 396023.0625 * 1024),
+    "bwd_causal_bf16_d512": (_BWD, "6e982fcd75cec507", 1000050.78125 * 2 * 1024, 446495.171875 * 1024),
     "prefill_causal_bf16_poly": (_PIPE, "b950ecf36dbe34db", 266960.84375 * 2 * 1024, 133123.546875 * 1024),
     "fp8_p8_outlier": (_P8, "40c93540ee3a0f74", 169015.1875 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_outlier": (_P8, "40c93540ee3a0f74", 122964.25 * 2 * 1024, 99840.0 * 1024),
