@@ -212,6 +212,34 @@ def test_splitd_scale_variants(D):
                 scales(qq, kk, vv, sc, True, Oref, Lref, fp8_codes(w, inp)))
 
 
+SWEEP_D = ([(D, "bf16") for D in range(32, 1025, 32)] + [(D, "f32") for D in range(32, 129, 32)]
+           + [(D, "fp8") for D in range(64, 257, 64)])
+
+
+@pytest.mark.parametrize("D,dt", SWEEP_D, ids=lambda x: str(x))
+def test_every_head_dim(D, dt):
+    """Every head dim the boundary accepts, on one ragged GQA shape: 97 query
+    rows and 130 keys (a partial query tile and a partial key tile in every
+    kernel's tiling), causal on every other D so both mask paths run; the
+    negative scale sends the call to the generic kernels (tiled up to 256,
+    four-wave split-D above)."""
+    causal = (D // 32) % 2 == 1
+    fp8 = dict(outlier_frac=0.01) if dt == "fp8" else {}
+    vs = dict(value_scale=0.5) if D > 256 else {}
+    w = Workload("sweep", 1, 4, 2, 97, 130, D, causal, dt, seed=1000 + D, **fp8, **vs)
+    full_parity(w)
+    if dt == "bf16" and D % 64 == 32:
+        note(f"sweep D={D} scale=-0.04")
+        inp = make_inputs(w)
+        q, k, v = (t.cuda() for t in inp)
+        o, lse = A.fwd(q, k, v, causal=causal, scale=-0.04)
+        torch.cuda.synchronize()
+        qq, kk, vv = oracle_inputs(w, inp)
+        Oref, Lref = oracle.attention(qq, kk, vv, -0.04, causal)
+        compare(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), Oref, Lref,
+                scales(qq, kk, vv, -0.04, causal, Oref, Lref, None))
+
+
 GROWING = [
     # (B, Hq, Hkv, Nq, Nkv, D, causal)
     (1, 2, 1, 150, 300, 1024, False),
