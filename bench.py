@@ -14,10 +14,10 @@ first runs below, then above, the clock it settles at under sustained load,
 and the timed steps should see the settled clock (the ZYFA article, "What the
 numbers establish, and where they overstate", makes the same point about
 sustained clocks).  Exactly --steps steps are timed (without --steps: about
-1 s of work).  The shader clock is sampled through amdsmi during the last
-part of the warm-up and the timed loop; the JSON line reports it, the
-percentage of the peak normalised to it, and the median, best, first and last
-per-launch times.
+1 s of work).  The shader clock and the socket power are sampled through
+amdsmi during the last part of the warm-up and the timed loop; the JSON line
+reports them, the percentage of the peak normalised to the clock, and the
+median, best, first and last per-launch times.
 
 Throughput is matmul TFLOP/s: 4 * B * Hq * D * (visible query/key pairs) per
 step (the QK^T and PV products; softmax work is not counted).  The roofline
@@ -122,9 +122,10 @@ def measured_traffic(name):
 
 
 class ClockSampler:
-    """Samples the GPU's current shader (gfx) clock in a background thread
-    through amdsmi, every `period` seconds, between start() and stop().
-    Reports nothing (None) where amdsmi or the metric is unavailable."""
+    """Samples the GPU's current shader (gfx) clock and socket power in a
+    background thread through amdsmi, every `period` seconds, between start()
+    and stop().  Reports nothing (None) where amdsmi or the metric is
+    unavailable."""
 
     def __init__(self, period=0.01, enabled=True):
         import threading
@@ -148,27 +149,30 @@ class ClockSampler:
             self.error = f"amdsmi unavailable: {type(e).__name__}"
 
     def _read(self):
+        """(gfx clock in MHz or None, socket power in W or None)."""
         smi = self._smi
         try:
             m = smi.amdsmi_get_gpu_metrics_info(self._handle)
+            pw = m.get("current_socket_power")
+            pw = float(pw) if isinstance(pw, (int, float)) and 0 < pw < 5000 else None
             clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
             if clks:
-                return float(np.mean(clks))  # the XCDs' clocks (all busy under these kernels)
+                return float(np.mean(clks)), pw  # the XCDs' clocks (all busy under these kernels)
             c = m.get("current_gfxclk")
             if isinstance(c, (int, float)) and 0 < c < 10000:
-                return float(c)
+                return float(c), pw
         except Exception:
             pass
         info = smi.amdsmi_get_clock_info(self._handle, smi.AmdSmiClkType.GFX)
         c = info.get("clk")
-        return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+        return (float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None), None
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                c = self._read()
+                c, pw = self._read()
                 if c is not None:
-                    self.samples.append((time.perf_counter(), c))
+                    self.samples.append((time.perf_counter(), c, pw))
             except Exception as e:  # pragma: no cover
                 self.error = f"amdsmi read failed: {type(e).__name__}"
                 return
@@ -198,16 +202,21 @@ class ClockSampler:
         and the timed loop read the idle clock, hence the window."""
         if not self.samples:
             return None
-        t = np.asarray([a for a, _ in self.samples])
-        c = np.asarray([b for _, b in self.samples])
+        t = np.asarray([a for a, _, _ in self.samples])
+        c = np.asarray([b for _, b, _ in self.samples])
+        pw = np.asarray([np.nan if x is None else x for _, _, x in self.samples], dtype=np.float64)
         inside = (t >= t0) & (t <= t1) if t0 is not None and t1 is not None else np.ones(len(c), bool)
         window = "the timed loop"
         if not inside.any():
             inside, window = np.ones(len(c), bool), "the last 0.5 s of warm-up and the timed loop"
         s = c[inside]
+        p = pw[inside]
+        p = p[np.isfinite(p)]
         return {"median_mhz": round(float(np.median(s)), 1), "min_mhz": round(float(s.min()), 1),
                 "max_mhz": round(float(s.max()), 1), "samples": int(s.size),
-                "source": f"amdsmi current gfx clock (mean over XCDs), sampled every 10 ms, over {window}"}
+                "socket_power_w": round(float(np.median(p)), 1) if p.size else None,
+                "source": f"amdsmi current gfx clock (mean over XCDs) and socket power, sampled every 10 ms, "
+                          f"over {window}"}
 
 
 def cpu_model():

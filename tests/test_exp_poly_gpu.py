@@ -54,6 +54,30 @@ def test_exp_poly_parity(case):
     assert d <= 2.0 ** -7
 
 
+@pytest.mark.parametrize("case", [(1, 2, 1, 150, 300, 128, False), (1, 2, 2, 200, 200, 128, True),
+                                  (1, 2, 2, 130, 260, 64, True)], ids=lambda c: "x".join(map(str, c)))
+def test_exp_poly_growing_scores(case):
+    """Scores that grow by a quarter per key (channel 0: 4 in every query, a
+    j in key j): the rescale path runs on (almost) every 64-key tile."""
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    note(f"fwd_exp_poly growing {case}")
+    w = Workload("polygrow", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", value_scale=0.5, seed=Nkv)
+    q, k, v = make_inputs(w)
+    q, k = q.float(), k.float()
+    q[..., 0] = 4.0
+    k[..., 0] = (D ** 0.5 / 16.0) * torch.arange(Nkv, dtype=torch.float32)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    O, L = A.fwd_exp_poly(*(t.cuda() for t in (q, k, v)), causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O, L = O.float().cpu().numpy(), L.cpu().numpy()
+    Oref, Lref = oracle.attention(*(t.to(torch.float64).numpy() for t in (q, k, v)), w.scale, causal)
+    assert np.isfinite(O).all()
+    assert np.abs(O - Oref).max() <= 2e-2
+    fin = np.isfinite(Lref)
+    assert np.array_equal(np.isneginf(L), ~fin)
+    assert (np.abs(L[fin] - Lref[fin]) / np.maximum(1.0, np.abs(Lref[fin]))).max() <= 1e-3
+
+
 def test_exp_poly_full_size_sampled():
     w = WORKLOADS["prefill_causal_bf16"]
     note(f"{w.name} polynomial exp, full size")

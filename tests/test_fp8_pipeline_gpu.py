@@ -29,6 +29,7 @@ Bars:
     rotating Q and K lowers it further to at most 0.7x of block scales alone
     (the oracle gives 0.32-0.53x and 0.39-0.50x over seeds 0-3).
 """
+import math
 import sys
 
 import numpy as np
@@ -37,6 +38,7 @@ import torch
 
 import oracle
 from fp8_bounds import ordinal, rotated_code_intervals
+from growing import growing_e4m3
 from exact_io_aware_attn_amd import attn as A
 from exact_io_aware_attn_amd.inputs import WORKLOADS, Workload, block_descales, make_inputs, quantize_e4m3
 
@@ -167,6 +169,33 @@ def test_blocks_attention_parity(case):
     O, L = A.fwd_fp8_blocks(*dev, *ddev, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     Oref, Lref = oracle.attention(*exact, scale=w.scale, causal=causal)
+    O = O.float().cpu().numpy()
+    assert np.isfinite(O).all()
+    err = np.abs(O - Oref).max()
+    assert err <= TOL_FP8, f"max |dO| = {err:.3e}"
+    check_lse(L.cpu().numpy(), Lref)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 2, 150, 150, 128, True, 0.25), (1, 2, 1, 200, 300, 128, False, 0.1),
+                                  (1, 2, 2, 200, 300, 64, True, 0.25), (1, 2, 2, 100, 190, 256, True, 0.1)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_blocks_growing_scores(case):
+    """Block descales on scores that rise along the key axis: the rescale
+    decision bounds the tile sum of the probabilities without the V block
+    factor folded into them, and the K block factor changes the exponent's
+    multiplier from one 64-key tile to the next."""
+    B, Hq, Hkv, Nq, Nkv, D, causal, gain = case
+    note(f"fwd_fp8_blocks growing {case}")
+    q8, k8, v8, base = growing_e4m3(B, Hq, Hkv, Nq, Nkv, D, gain, seed=Nkv + D)
+    rng = np.random.default_rng(Nq)
+    ds = [(rng.uniform(0.5, 2.0, size=(B, H, (N + 63) // 64)) * d).astype(np.float32)
+          for d, H, N in zip(base, (Hq, Hkv, Hkv), (Nq, Nkv, Nkv))]
+    exact = [oracle.dequantize_blocks(t.view(torch.uint8).numpy(), d) for t, d in zip((q8, k8, v8), ds)]
+    scale = 1.0 / math.sqrt(D)
+    O, L = A.fwd_fp8_blocks(*(t.cuda() for t in (q8, k8, v8)), *(torch.from_numpy(d).cuda() for d in ds),
+                            causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention(*exact, scale=scale, causal=causal)
     O = O.float().cpu().numpy()
     assert np.isfinite(O).all()
     err = np.abs(O - Oref).max()

@@ -23,6 +23,7 @@ import torch
 
 import oracle
 from bars import TOL_O, bar_violations, scales, scales_head
+from growing import growing_e4m3
 from exact_io_aware_attn_amd import attn as A
 from exact_io_aware_attn_amd.inputs import WORKLOADS, Workload, make_inputs
 
@@ -271,6 +272,38 @@ def test_growing_scores_parity(case):
     qq, kk, vv = oracle_inputs(w, inp)
     Oref, Lref = oracle.attention(qq, kk, vv, w.scale, causal)
     compare(w, O, L, Oref, Lref, scales(qq, kk, vv, w.scale, causal, Oref, Lref, None))
+
+
+GROWING_FP8 = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal, gain): 0.25 per key moves the row
+    # maximum by about 23 (base 2) per 64-key tile, past the tile-sum bound on
+    # every tile; 0.1 by about 9, under it, so the probabilities are kept
+    # with a stale maximum and grow to about 2^9
+    (1, 2, 1, 150, 150, 128, False, 0.25),
+    (1, 2, 2, 150, 150, 128, True, 0.25),
+    (1, 2, 2, 200, 300, 128, True, 0.1),
+    (1, 2, 1, 120, 140, 64, False, 0.25),
+    (1, 2, 2, 200, 300, 64, True, 0.1),
+    (1, 2, 2, 100, 110, 256, True, 0.25),
+    (1, 2, 1, 150, 300, 256, False, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", GROWING_FP8, ids=lambda c: "Nq{}_Nkv{}_D{}_{}_g{}".format(
+    *c[3:6], "causal" if c[6] else "full", c[7]))
+def test_growing_scores_fp8(case):
+    """The e4m3 kernels' rescale path (taken when a lane's tile sum of the
+    probabilities passes the bound, the tile maximum then replacing the
+    running one) and their stale-maximum path, on scores that rise along
+    the key axis."""
+    B, Hq, Hkv, Nq, Nkv, D, causal, gain = case
+    w = Workload("growing8", B, Hq, Hkv, Nq, Nkv, D, causal, "fp8", seed=D + Nkv)
+    note(f"growing e4m3 B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal} gain={gain}")
+    inp = growing_e4m3(B, Hq, Hkv, Nq, Nkv, D, gain, seed=D + Nkv)
+    O, L = run_gpu(w, inp, guard=64)
+    qq, kk, vv = oracle_inputs(w, inp)
+    Oref, Lref = oracle.attention(qq, kk, vv, w.scale, causal)
+    compare(w, O, L, Oref, Lref, scales(qq, kk, vv, w.scale, causal, Oref, Lref, fp8_codes(w, inp)))
 
 
 FP8_SMALL = [
