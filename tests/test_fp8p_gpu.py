@@ -22,6 +22,7 @@ Parity, two ways:
 Accuracy against exact attention: the e4m3-P error within e4m3 precision of
 O's scale, Lean P's error 1-2x it (the article documents 1.22-1.36x).
 """
+import functools
 import sys
 
 import numpy as np
@@ -180,30 +181,41 @@ def test_fp8p_parity_real_inputs(case, lean):
     note(f"  worst |dO| / admissible {worst:.3f}; open decisions {np.mean(amb):.4f}")
 
 
-@pytest.mark.parametrize("lean", [False, True], ids=["exact", "lean"])
-def test_fp8p_full_size_sampled(lean):
-    """The benchmarked problem (24 x 16K x 16K, D = 128, outlier channels)
-    in the launch configuration the bench times, on sampled rows: the
-    boundary-aware parity against the float64 oracle, and the accuracy
-    against exact attention."""
-    w = WORKLOADS["fp8_outlier"]
+@functools.lru_cache(maxsize=1)
+def full_size_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed, outlier_frac):
+    """make_inputs of a full-size workload, kept for the next test on the
+    same inputs (the exact and Lean variants of one problem)."""
+    return make_inputs(Workload("full", B, Hq, Hkv, Nq, Nkv, D, False, dtype, seed=seed, outlier_frac=outlier_frac))
+
+
+@pytest.mark.parametrize("name,lean", [("fp8_outlier", False), ("fp8_outlier", True),
+                                       ("fp8_p8_causal_32k", False), ("fp8_lean_causal_32k", True)],
+                         ids=["outlier_exact", "outlier_lean", "causal32k_exact", "causal32k_lean"])
+def test_fp8p_full_size_sampled(name, lean):
+    """The benchmarked problems (24 x 16K x 16K with outlier channels; the
+    32K-token causal prefill of 32 heads) in the launch configuration the
+    bench times, on sampled rows: the boundary-aware parity against the
+    float64 oracle, and the accuracy against exact attention."""
+    w = WORKLOADS[name]
     note(f"{w.name} e4m3 P lean={lean}, full size")
-    q8, k8, v8, desc = make_inputs(w)
-    qc, kc = (oracle.e4m3fn_decode(t.view(torch.uint8).numpy()) for t in (q8, k8))
-    vv = oracle.e4m3fn_decode(v8.view(torch.uint8).numpy()) * np.float64(desc[2])
+    q8, k8, v8, desc = full_size_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, w.seed, w.outlier_frac)
     dev = [t.cuda() for t in (q8, k8, v8)]
     ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda:0") for d in desc]
     O, L = run(w, dev, ds, lean)
     assert np.isfinite(O).all() and np.isfinite(L).all()
+    decode = lambda t: oracle.e4m3fn_decode(t.view(torch.uint8).numpy())
+    G = w.Hq // w.Hkv
     rng = np.random.default_rng(3)
     err_x, scale, worst, amb = [], [], 0.0, []
     for hq in [0, w.Hq - 1] + [int(x) for x in rng.integers(0, w.Hq, 2)]:
         rows = np.unique(np.concatenate([[0, w.Nq - 1], rng.integers(0, w.Nq, 16)]))
-        r, a = check_bounded(O[0, hq][rows].astype(np.float64), L[0, hq][rows].astype(np.float64), qc[0, hq],
-                             kc[0, hq], vv[0, hq], desc[0], desc[1], w.scale, w.causal, lean, rows)
+        qc, kc = decode(q8[0, hq]), decode(k8[0, hq // G])
+        vv = decode(v8[0, hq // G]) * np.float64(desc[2])
+        r, a = check_bounded(O[0, hq][rows].astype(np.float64), L[0, hq][rows].astype(np.float64), qc, kc, vv,
+                             desc[0], desc[1], w.scale, w.causal, lean, rows)
         worst, amb = max(worst, r), amb + [a]
-        Ox, _ = oracle.attention_head(qc[0, hq] * np.float64(desc[0]), kc[0, hq] * np.float64(desc[1]), vv[0, hq],
-                                      w.scale, w.causal, rows=rows)
+        Ox, _ = oracle.attention_head(qc * np.float64(desc[0]), kc * np.float64(desc[1]), vv, w.scale, w.causal,
+                                      rows=rows)
         err_x.append(O[0, hq][rows] - Ox)
         scale.append(Ox)
     rms = lambda a: float(np.sqrt((np.concatenate(a) ** 2).mean()))
