@@ -63,12 +63,15 @@ def check(O, L, Oref, Lref, label):
     assert not bad, f"{label}: " + "; ".join(bad)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,Nq,causal", [(128, 2, 1, 100, True), (1024, 1, 1, 70, False)],
-                         ids=["d128_gqa_causal", "d1024"])
+@pytest.mark.parametrize("D,Hq,Hkv,Nq,causal", [(128, 2, 1, 100, True), (320, 1, 1, 70, False),
+                                                 (512, 2, 1, 40, True), (768, 2, 1, 70, False),
+                                                 (1024, 1, 1, 70, False)],
+                         ids=["d128_gqa_causal", "d320", "d512_gqa_causal", "d768_gqa", "d1024"])
 def test_longest_key_slab(D, Hq, Hkv, Nq, causal):
-    """K and V slabs of 2^31 - 2 D bytes (8 388 607 keys at D = 128, 1 048 575
-    at D = 1024): the bf16 kernel (a two-work-group grid, 64-key tiles) and
-    the eight-wave split-D kernel stream every key tile up to the limit."""
+    """K and V slabs of 2^31 - 2 D bytes (8 388 607 keys at D = 128 down to
+    1 048 575 at D = 1024): the bf16 kernel (a small grid, 64-key tiles), the
+    wide-head kernel (64-key tiles at D = 320, 32 at 512), the four-wave and
+    the eight-wave split-D kernels stream every key tile up to the limit."""
     Nkv = max_rows(D)
     note(f"longest key slab: B=1 Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal}")
     dev = torch.device("cuda:0")
@@ -132,4 +135,46 @@ def test_longest_query_slab():
     for h in range(Hq):
         Oref, Lref = oracle.attention_head(q[0, h, rt].double().cpu().numpy(), k[0, h].double().cpu().numpy(),
                                            v[0, h].double().cpu().numpy(), scale, False)
+        check(o[0, h, rt].double().cpu().numpy(), lse[0, h, rt].double().cpu().numpy(), Oref, Lref, f"head {h}")
+
+
+def test_longest_key_slab_e4m3():
+    """e4m3 K and V slabs of 2^31 - 128 bytes (16 777 215 keys at D = 128,
+    one byte per element): the direct-to-LDS kernel's K tiles and its
+    register-staged V rows up to the limit.  Codes: one-hot keys 1.0, value
+    rows of N(0, 1) draws rounded to e4m3, query code 352 on the marker's
+    channel (score 31 with unit descales)."""
+    D, Hq, Hkv, Nq = 128, 2, 1, 90
+    Nkv = (1 << 31) // D - 1
+    note(f"longest e4m3 key slab: B=1 Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal=True")
+    dev = torch.device("cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    marks = marker_keys(Nkv, 16)
+    M = len(marks)
+    g = torch.Generator(device=dev).manual_seed(3)
+    k = torch.zeros(1, Hkv, Nkv, D, dtype=torch.uint8, device=dev)
+    v = torch.zeros(1, Hkv, Nkv, D, dtype=torch.uint8, device=dev)
+    mk = torch.from_numpy(marks).to(dev)
+    k[0, 0, mk, torch.arange(M, device=dev)] = 0x38                     # e4m3 1.0
+    v[0, 0, mk] = torch.randn(M, D, generator=g, device=dev).to(torch.float8_e4m3fn).view(torch.uint8)
+    q = torch.zeros(1, Hq, Nq, D, dtype=torch.uint8, device=dev)
+    off = Nkv - Nq
+    for h in range(Hq):
+        for i in range(Nq):
+            vis = np.nonzero(marks <= i + off)[0]
+            m = int(vis[-1]) if h == 0 else int(vis[(5 * i + 1) % len(vis)])
+            q[0, h, i, m] = 0x7B                                          # e4m3 352
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    q8, k8, v8 = (t.view(torch.float8_e4m3fn) for t in (q, k, v))
+    o, lse = A.fwd_fp8(q8, k8, v8, one, one, one, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, Nq // 2, Nq - 2, Nq - 1])
+    rt = torch.from_numpy(rows).to(dev)
+    # the oracle's decoding of every code, applied by table lookup (two
+    # billion codes per tensor)
+    table = oracle.e4m3fn_decode(np.arange(256, dtype=np.uint8))
+    kh = table[k[0, 0].cpu().numpy()]
+    vh = table[v[0, 0].cpu().numpy()]
+    for h in range(Hq):
+        Oref, Lref = oracle.attention_head(table[q[0, h].cpu().numpy()], kh, vh, scale, True, rows=rows)
         check(o[0, h, rt].double().cpu().numpy(), lse[0, h, rt].double().cpu().numpy(), Oref, Lref, f"head {h}")
