@@ -41,9 +41,10 @@ def note(msg):
     print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
 
 
-def max_rows(D):
-    """Largest row count whose bf16 slab stays below 2^31 bytes."""
-    return (1 << 30) // D - 1
+def max_rows(D, elt=2):
+    """Largest row count whose slab of elt-byte elements stays below 2^31
+    bytes."""
+    return (1 << 31) // (elt * D) - 1
 
 
 def marker_keys(Nkv, n):
@@ -57,37 +58,42 @@ def marker_keys(Nkv, n):
     return np.asarray(keys, dtype=np.int64)
 
 
-def check(O, L, Oref, Lref, label):
-    bad = bar_violations(O, L, Oref, Lref, "bf16", scale_aware=False)
+def check(O, L, Oref, Lref, label, dt="bf16"):
+    bad = bar_violations(O, L, Oref, Lref, dt, scale_aware=False)
     note(f"  {label}: max |dO| = {np.abs(O - Oref).max():.3e}")
     assert not bad, f"{label}: " + "; ".join(bad)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,Nq,causal", [(128, 2, 1, 100, True), (320, 1, 1, 70, False),
-                                                 (512, 2, 1, 40, True), (768, 2, 1, 70, False),
-                                                 (1024, 1, 1, 70, False)],
-                         ids=["d128_gqa_causal", "d320", "d512_gqa_causal", "d768_gqa", "d1024"])
-def test_longest_key_slab(D, Hq, Hkv, Nq, causal):
-    """K and V slabs of 2^31 - 2 D bytes (8 388 607 keys at D = 128 down to
-    1 048 575 at D = 1024): the bf16 kernel (a small grid, 64-key tiles), the
-    wide-head kernel (64-key tiles at D = 320, 32 at 512), the four-wave and
-    the eight-wave split-D kernels stream every key tile up to the limit."""
-    Nkv = max_rows(D)
-    note(f"longest key slab: B=1 Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal}")
+@pytest.mark.parametrize("D,Hq,Hkv,Nq,causal,dt", [(128, 2, 1, 100, True, "bf16"), (320, 1, 1, 70, False, "bf16"),
+                                                    (512, 2, 1, 40, True, "bf16"), (768, 2, 1, 70, False, "bf16"),
+                                                    (1024, 1, 1, 70, False, "bf16"), (96, 2, 2, 50, True, "bf16"),
+                                                    (128, 1, 1, 70, False, "f32")],
+                         ids=["d128_gqa_causal", "d320", "d512_gqa_causal", "d768_gqa", "d1024", "d96_tiled",
+                              "f32_d128_tiled"])
+def test_longest_key_slab(D, Hq, Hkv, Nq, causal, dt):
+    """K and V slabs just below 2^31 bytes (8 388 607 bf16 keys at D = 128
+    down to 1 048 575 at D = 1024): the bf16 kernel (a small grid, 64-key
+    tiles), the wide-head kernel (64-key tiles at D = 320, 32 at 512), the
+    four-wave and the eight-wave split-D kernels, and the generic tiled
+    kernel (bf16 D = 96, fp32) stream every key tile up to the limit."""
+    elt = 4 if dt == "f32" else 2
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    Nkv = max_rows(D, elt)
+    note(f"longest key slab: B=1 Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal} {dt}")
     dev = torch.device("cuda:0")
     scale = 1.0 / math.sqrt(D)
     marks = marker_keys(Nkv, min(D, 16))
     M = len(marks)
     g = torch.Generator(device=dev).manual_seed(D)
-    k = torch.zeros(1, Hkv, Nkv, D, dtype=torch.bfloat16, device=dev)
-    v = torch.zeros(1, Hkv, Nkv, D, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, Hkv, Nkv, D, dtype=tdt, device=dev)
+    v = torch.zeros(1, Hkv, Nkv, D, dtype=tdt, device=dev)
     mk = torch.from_numpy(marks).to(dev)
     for h in range(Hkv):
         k[0, h, mk, torch.arange(M, device=dev)] = 1.0
-        v[0, h, mk] = torch.randn(M, D, generator=g, device=dev).to(torch.bfloat16)
+        v[0, h, mk] = torch.randn(M, D, generator=g, device=dev).to(tdt)
     # query i of head h picks a marker it can see: the last one visible
     # (head 0) or another visible one (head 1)
-    q = torch.zeros(1, Hq, Nq, D, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros(1, Hq, Nq, D, dtype=tdt, device=dev)
     off = Nkv - Nq
     for h in range(Hq):
         for i in range(Nq):
@@ -105,7 +111,7 @@ def test_longest_key_slab(D, Hq, Hkv, Nq, causal):
                                            rows=rows)
         O = o[0, h, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
         L = lse[0, h, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
-        check(O, L, Oref, Lref, f"head {h}")
+        check(O, L, Oref, Lref, f"head {h}", dt)
 
 
 def test_longest_query_slab():
@@ -145,7 +151,7 @@ def test_longest_key_slab_e4m3():
     rows of N(0, 1) draws rounded to e4m3, query code 352 on the marker's
     channel (score 31 with unit descales)."""
     D, Hq, Hkv, Nq = 128, 2, 1, 90
-    Nkv = (1 << 31) // D - 1
+    Nkv = max_rows(D, 1)
     note(f"longest e4m3 key slab: B=1 Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal=True")
     dev = torch.device("cuda:0")
     scale = 1.0 / math.sqrt(D)
