@@ -274,6 +274,42 @@ def test_growing_scores_parity(case):
     compare(w, O, L, Oref, Lref, scales(qq, kk, vv, w.scale, causal, Oref, Lref, None))
 
 
+LARGE = [
+    # (B, Hq, Hkv, Nq, Nkv, D, causal): every kernel family (bf16 64/128, the
+    # wide kernel, both split-D kernels, the tiled kernel at D = 96)
+    (1, 2, 1, 150, 300, 128, True),
+    (1, 2, 2, 200, 150, 64, False),
+    (1, 2, 1, 130, 200, 256, True),
+    (1, 2, 2, 100, 120, 512, False),
+    (1, 2, 1, 90, 100, 768, True),
+    (1, 2, 2, 70, 100, 1024, False),
+    (1, 2, 2, 120, 140, 96, True),
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=lambda c: "Nq{}_Nkv{}_D{}_{}".format(*c[3:6], "causal" if c[6] else "full"))
+def test_large_scores_parity(case):
+    """Scores of standard deviation 900 (Q and K times 30): each row's
+    weight sits on one or two keys, scores three thousand units apart meet
+    in one tile, and a running maximum far below the new one makes exp2
+    overflow to inf before the rescale decision; the rescale must then
+    replace it, and keyless-row and masked paths keep their -inf.  The
+    stated bars only (2e-2 on O, 1e-3 x |LSE| on LSE): the rows are one- or
+    two-hot with |O| of order 1, where a wrong rescale shows at once, and
+    the float32 sums of scores near 3000 move LSE by about 1e-3, beyond the
+    5e-4 absolute scale-aware bar that is set for scores of order 1."""
+    B, Hq, Hkv, Nq, Nkv, D, causal = case
+    w = Workload("large", B, Hq, Hkv, Nq, Nkv, D, causal, "bf16", seed=D + Nq)
+    note(f"large scores B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} causal={causal}")
+    q, k, v = make_inputs(w)
+    inp = ((q.float() * 30).to(torch.bfloat16), (k.float() * 30).to(torch.bfloat16), v)
+    O, L = run_gpu(w, inp, guard=64)
+    qq, kk, vv = oracle_inputs(w, inp)
+    Oref, Lref = oracle.attention(qq, kk, vv, w.scale, causal)
+    bad = bar_violations(O, L, Oref, Lref, "bf16", scale_aware=False)
+    assert not bad, "; ".join(bad)
+
+
 GROWING_FP8 = [
     # (B, Hq, Hkv, Nq, Nkv, D, causal, gain): 0.25 per key moves the row
     # maximum by about 23 (base 2) per 64-key tile, past the tile-sum bound on
