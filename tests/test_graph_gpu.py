@@ -1,0 +1,204 @@
+"""Calls captured into a HIP graph, and calls on a side stream.
+
+The entry points allocate nothing, keep no per-shape host state, enqueue
+only kernels (no memset, no copy, no host synchronisation) and read e4m3
+descales from device memory (ZYFA article, "Getting started with ZYFA": a
+call never waits on the host, so it can run under graph capture).  Each
+case captures one call (or one pipeline of calls) on static buffers into a
+torch.cuda.CUDAGraph, then replays it three times; before each replay new
+inputs are copied into the static ones and the same call runs eagerly into
+separate buffers, and the replay must equal that eager result bit for bit
+(the kernels are deterministic).  The e4m3 cases also change the device
+descales between replays, so a replay that had baked in the captured values
+would fail.
+"""
+import math
+import sys
+
+import pytest
+import torch
+
+from exact_io_aware_attn_amd import attn as A
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def randn(shape, g, scale=1.0):
+    return torch.randn(shape, generator=g, device=DEV) * scale
+
+
+def qkv(B, Hq, Hkv, Nq, Nkv, D, dt, g):
+    q = randn((B, Hq, Nq, D), g).to(dt)
+    k = randn((B, Hkv, Nkv, D), g).to(dt)
+    v = randn((B, Hkv, Nkv, D), g).to(dt)
+    return [q, k, v]
+
+
+def e4m3(shape, g):
+    return (randn(shape, g) * 8).to(torch.float8_e4m3fn)
+
+
+def descales(g):
+    return [(0.05 + torch.rand(1, generator=g, device=DEV) * 0.1).float() for _ in range(3)]
+
+
+# Each case: make(seed) -> list of input tensors; outs(ins) -> static output
+# tensors; call(ins, outs) -> runs the entry point(s) writing into outs.
+
+def fwd_case(D, dt, causal, B=1, Hq=4, Hkv=2, Nq=300, Nkv=333):
+    def make(seed):
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        return qkv(B, Hq, Hkv, Nq, Nkv, D, dt, g)
+
+    def outs(ins):
+        return [torch.empty_like(ins[0]), torch.empty(B, Hq, Nq, device=DEV)]
+
+    def call(ins, o):
+        A.fwd(*ins, causal=causal, out=o[0], lse=o[1])
+    return make, outs, call
+
+
+def fp8_case(kind, D=128, causal=True, B=1, Hq=4, Hkv=2, Nq=300, Nkv=333):
+    def make(seed):
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        return [e4m3((B, Hq, Nq, D), g), e4m3((B, Hkv, Nkv, D), g), e4m3((B, Hkv, Nkv, D), g)] + descales(g)
+
+    def outs(ins):
+        return [torch.empty(B, Hq, Nq, D, dtype=torch.bfloat16, device=DEV), torch.empty(B, Hq, Nq, device=DEV)]
+
+    def call(ins, o):
+        if kind == "fp8":
+            A.fwd_fp8(*ins[:3], *ins[3:], causal=causal, out=o[0], lse=o[1])
+        else:
+            A.fwd_fp8_p(*ins[:3], *ins[3:], causal=causal, lean=kind == "lean", out=o[0], lse=o[1])
+    return make, outs, call
+
+
+def poly_case(D=128, B=1, Hq=4, Hkv=2, Nq=300, Nkv=333):
+    make, outs, _ = fwd_case(D, torch.bfloat16, True, B, Hq, Hkv, Nq, Nkv)
+
+    def call(ins, o):
+        A.fwd_exp_poly(*ins, causal=True, out=o[0], lse=o[1])
+    return make, outs, call
+
+
+def splitkv_case(noalloc, n_splits=4, D=128, B=1, Hq=4, Hkv=2, Nq=100, Nkv=1000):
+    make, outs0, _ = fwd_case(D, torch.bfloat16, True, B, Hq, Hkv, Nq, Nkv)
+    ws = torch.empty(A.splitkv_workspace_bytes(B, Hq, Nq, D, n_splits), dtype=torch.uint8, device=DEV)
+
+    def call(ins, o):
+        if noalloc:
+            A.fwd_splitkv_noalloc(*ins, n_splits, causal=True, out=o[0], lse=o[1])
+        else:
+            A.fwd_splitkv(*ins, n_splits, causal=True, workspace=ws, out=o[0], lse=o[1])
+    return make, outs0, call
+
+
+def pipeline_case(D=128, B=1, H=2, N=200):
+    # bf16 Q, K, V -> block e4m3 codes (Q and K rotated) -> block-scaled attention
+    codes = [torch.empty(B, H, N, D, dtype=torch.float8_e4m3fn, device=DEV) for _ in range(3)]
+    desc = [torch.empty(B, H, (N + 63) // 64, device=DEV) for _ in range(3)]
+
+    def make(seed):
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        signs = (torch.randint(0, 2, (D,), generator=g, device=DEV) * 2 - 1).to(torch.int8)
+        return qkv(B, H, H, N, N, D, torch.bfloat16, g) + [signs]
+
+    def outs(ins):
+        return [torch.empty(B, H, N, D, dtype=torch.bfloat16, device=DEV), torch.empty(B, H, N, device=DEV)]
+
+    def call(ins, o):
+        for i in range(3):
+            A.quantize_fp8(ins[i], ins[3] if i < 2 else None, codes=codes[i], descales=desc[i])
+        A.fwd_fp8_blocks(*codes, *desc, causal=True, out=o[0], lse=o[1])
+    return make, outs, call
+
+
+def bwd_case(D, B=1, Hq=4, Hkv=2, N=200):
+    ws = torch.empty(A.bwd_workspace_bytes(B, Hq, N), dtype=torch.uint8, device=DEV)
+
+    def make(seed):
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        q, k, v = qkv(B, Hq, Hkv, N, N, D, torch.bfloat16, g)
+        o, lse = A.fwd(q, k, v, causal=True)   # the forward outputs are inputs of the backward
+        return [q, k, v, o, lse, randn((B, Hq, N, D), g).to(torch.bfloat16)]
+
+    def outs(ins):
+        return [torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2])]
+
+    def call(ins, o):
+        A.bwd(*ins, causal=True, workspace=ws, dq=o[0], dk=o[1], dv=o[2])
+    return make, outs, call
+
+
+CASES = {
+    "bf16_d128": lambda: fwd_case(128, torch.bfloat16, True),
+    "bf16_d64_full": lambda: fwd_case(64, torch.bfloat16, False),
+    "bf16_d512_wide": lambda: fwd_case(512, torch.bfloat16, True, Nq=130, Nkv=150),
+    "bf16_d768_splitd": lambda: fwd_case(768, torch.bfloat16, False, Nq=130, Nkv=150),
+    "bf16_d1024_splitd8": lambda: fwd_case(1024, torch.bfloat16, True, Nq=130, Nkv=150),
+    "bf16_d96_tiled": lambda: fwd_case(96, torch.bfloat16, True),
+    "f32_d64_tiled": lambda: fwd_case(64, torch.float32, False),
+    "fp8_descales": lambda: fp8_case("fp8"),
+    "fp8_p_e4m3": lambda: fp8_case("e4m3"),
+    "fp8_p_lean": lambda: fp8_case("lean"),
+    "exp_poly": poly_case,
+    "splitkv_workspace": lambda: splitkv_case(False),
+    "splitkv_noalloc": lambda: splitkv_case(True),
+    "fp8_pipeline": pipeline_case,
+    "bwd_d128": lambda: bwd_case(128),
+    "bwd_d256": lambda: bwd_case(256),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_graph_replays_match_eager(name):
+    note(f"graph capture: {name}")
+    make, outs, call = CASES[name]()
+    ins = make(0)
+    o = outs(ins)
+    call(ins, o)                       # eager first: library loaded, scratch address taken
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(ins, o)
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        new = make(r)
+        for s, n in zip(ins, new):
+            s.copy_(n)
+        ref = outs(ins)
+        call(ins, ref)                 # eager work between the replays
+        torch.cuda.synchronize()
+        for t in o:
+            t.fill_(float("nan")) if t.is_floating_point() else t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(o, ref)):
+            assert torch.equal(a, b), f"{name}: replay {r}, output {j} differs from the eager call"
+    del graph
+
+
+def test_side_stream_matches_default_stream():
+    """A call on a non-default stream, ordered after the stream that made its
+    inputs by an event, equals the same call on the default stream."""
+    g = torch.Generator(device=DEV).manual_seed(11)
+    side = torch.cuda.Stream()
+    for D in (128, 512, 1024):
+        q, k, v = qkv(1, 4, 2, 200, 260, D, torch.bfloat16, g)
+        o0, l0 = A.fwd(q, k, v, causal=True)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            o1, l1 = A.fwd(q, k, v, causal=True)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), f"D={D}"
+        o2, l2 = A.fwd(q, k, v, causal=True, stream=side)
+        side.synchronize()
+        assert torch.equal(o0, o2) and torch.equal(l0, l2), f"D={D}, explicit stream"
