@@ -294,3 +294,34 @@ def test_noalloc_scratch_limit():
 @pytest.mark.skipif(_gpu_visible(), reason="a GPU is visible: the call would launch")
 def test_noalloc_without_device_returns_hip_error():
     assert noalloc() == A.ATTN_ERR_HIP
+
+
+def test_last_error_is_per_thread():
+    """attn_last_error describes the last failure on the calling thread: two
+    threads failing in different ways at the same time (ctypes releases the
+    interpreter lock around each call) each read back their own message, and
+    a thread that has not failed reads an empty string."""
+    import threading
+    L = A.lib()
+    errors = []
+    start = threading.Barrier(2)
+
+    def worker(kw, expect_status, expect_text):
+        try:
+            start.wait()
+            for _ in range(2000):
+                assert call(**kw) == expect_status
+                msg = L.attn_last_error().decode()
+                assert expect_text in msg, msg
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    t1 = threading.Thread(target=worker, args=(dict(D=48), A.ATTN_ERR_UNSUPPORTED, "D=48"))
+    t2 = threading.Thread(target=worker, args=(dict(Hq=6, Hkv=4), A.ATTN_ERR_INVALID_ARG, "Hq"))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert not errors, errors[0]
+
+    fresh = []
+    t3 = threading.Thread(target=lambda: fresh.append(L.attn_last_error()))
+    t3.start(); t3.join()
+    assert fresh == [b""]
