@@ -9,8 +9,9 @@
 //
 // Layout (the direct-to-LDS kernel's, attn_fwd_pipe.hip, which keeps the
 // e4m3 paths):
-//  * A work-group is 4 waves x 32 query rows; a wave owns its rows through
-//    every key tile.  Transposed products on the 32x32x16 bf16 matrix
+//  * A work-group is 4 waves x 32 query rows (8 waves, 256 rows, for large
+//    grids without the causal mask); a wave owns its rows through every key
+//    tile.  Transposed products on the 32x32x16 bf16 matrix
 //    instruction: S^T = K Q^T (A = K from LDS, B = Q held in registers) and
 //    O^T += V^T P^T (A = V^T from the transposing LDS read, B = P).  Lane l
 //    holds query l % 32 in both accumulators, so the S^T registers rounded
@@ -47,10 +48,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumMax = 65536.0f;  // per-lane tile sum that forces a rescale
 
-template <int D_, int BC_>
+template <int D_, int BC_, int NW_ = 4>
 struct Bf16Cfg {
   static constexpr int D = D_;
-  static constexpr int NW = 4;                  // waves per work-group
+  static constexpr int NW = NW_;                // waves per work-group (4 or 8)
   static constexpr int NT = NW * 64;
   static constexpr int QW = 32;                 // query rows per wave
   static constexpr int BR = NW * QW;            // query rows per work-group
@@ -70,9 +71,10 @@ struct Bf16Cfg {
   static_assert(LDS <= 64 * 1024, "two work-groups per CU at least");
 };
 
-template <int D, int BC>
-__global__ __launch_bounds__(256, (D == 128 && BC == 32) ? 3 : 2) void attn_fwd_bf16_kernel(FwdParams p) {
-  using C = Bf16Cfg<D, BC>;
+template <int D, int BC, int NW = 4>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : ((D == 128 && BC == 32) ? 3 : 2)) void attn_fwd_bf16_kernel(
+    FwdParams p) {
+  using C = Bf16Cfg<D, BC, NW>;
   // LDS: K slot 0, K slot 1, V slot 0, V slot 1
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   const uint32_t lds_base =
@@ -318,25 +320,34 @@ __global__ __launch_bounds__(256, (D == 128 && BC == 32) ? 3 : 2) void attn_fwd_
   }  // job
 }
 
-template <int D, int BC>
+template <int D, int BC, int NW = 4>
 hipError_t launch_bf16(const FwdParams& p0, hipStream_t stream) {
-  using C = Bf16Cfg<D, BC>;
+  using C = Bf16Cfg<D, BC, NW>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
   p.pair_causal = pair_causal_tiles(p);
   const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BC>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BC, NW>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 // D = 128: 32-key tiles at three waves per SIMD where the grid gives every
 // CU at least three work-groups, otherwise 64-key tiles at two (a grid too
 // small for the third slot gains nothing from the smaller tiles' extra
-// barriers).
+// barriers).  Without the causal mask, and where 256-row work-groups still
+// give every CU one, eight waves (256 query rows) share each 64-key K/V
+// tile: half the direct-to-LDS loads and L2-to-LDS bytes per product at
+// two waves per SIMD.  With the mask, a 256-row work-group loads diagonal
+// tiles that its first waves skip, and the four-wave layouts stay faster.
 hipError_t launch_bf16_d128(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;
+  if (!p.causal) {
+    const int64_t wide = (int64_t)p.n_splits * p.B * p.Hq * ((p.Nq + Bf16Cfg<128, 64, 8>::BR - 1) /
+                                                             Bf16Cfg<128, 64, 8>::BR);
+    if (wide >= (int64_t)cu_count()) return launch_bf16<128, 64, 8>(p0, stream);
+  }
   p.n_qtiles = (p.Nq + Bf16Cfg<128, 32>::BR - 1) / Bf16Cfg<128, 32>::BR;
   p.pair_causal = pair_causal_tiles(p);
   const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);

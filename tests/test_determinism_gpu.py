@@ -49,7 +49,8 @@ BF16 = [
     (1, 8, 2, 700, 901, 128, True),      # direct-to-LDS, 64-key tiles (small grid)
     (1, 64, 16, 2048, 2048, 128, True),  # 32-key tiles, 1024 work-groups, unpaired
     (2, 64, 16, 4096, 4096, 128, True),  # 32-key tiles, paired causal tiles
-    (1, 768, 192, 128, 100, 128, False),  # 32-key tiles, one query tile per head
+    (1, 768, 192, 128, 100, 128, False),  # eight waves, 64-key tiles, one query tile per head
+    (1, 64, 16, 1000, 3000, 128, False),  # eight waves, 64-key tiles, 256 work-groups
     (1, 8, 8, 1000, 1000, 64, True),     # direct-to-LDS, D = 64
     (1, 4, 2, 600, 777, 320, True),      # wide-head kernel, 64-key tiles
     (1, 4, 2, 600, 777, 512, False),     # wide-head kernel, 32-key tiles

@@ -125,13 +125,20 @@ SMALL = [
     (1, 4, 2, 600, 1000, 128, True, "bf16"),
     (2, 2, 1, 777, 777, 64, True, "bf16"),
     (1, 2, 2, 513, 1500, 128, False, "bf16"),
-    # grids of 768 work-groups (three per compute unit: 32-key tiles at three
-    # waves per SIMD) over few keys, so each key tile carries a large share
-    # of every row: keyless causal rows, a ragged last tile, MHA and GQA
+    # grids of 768 work-groups over few keys, so each key tile carries a
+    # large share of every row: causal, 32-key tiles at three waves per SIMD
+    # (keyless rows, a ragged last tile, MHA and GQA); without the mask,
+    # eight waves (256 query rows) per work-group and 64-key tiles
     (1, 768, 768, 128, 77, 128, True, "bf16"),
     (1, 768, 192, 100, 100, 128, True, "bf16"),
     (1, 768, 192, 128, 77, 128, False, "bf16"),
     (1, 768, 768, 100, 100, 128, False, "bf16"),
+    # eight-wave work-groups: ragged 256-row query tiles and 64-key tiles,
+    # GQA, one row per head
+    (1, 256, 64, 200, 300, 128, False, "bf16"),
+    (1, 128, 128, 600, 333, 128, False, "bf16"),
+    (2, 64, 16, 257, 77, 128, False, "bf16"),
+    (1, 256, 256, 1, 500, 128, False, "bf16"),
     # wide head dims: one or two key tiles only, keyless causal rows, tails
     (1, 2, 2, 64, 32, 320, False, "bf16"),
     (1, 2, 2, 129, 33, 256, False, "bf16"),
