@@ -87,10 +87,10 @@ MEASURED_TRAFFIC = {
     "prefill_causal_bf16": (_BF16, "ab3efdefb375db1a", 281431.3125 * 2 * 1024, 137430.453125 * 1024),
     "gqa_causal_bf16": (_BF16, "ab3efdefb375db1a", 200251.21875 * 2 * 1024, 137226.421875 * 1024),
     "gqa_cross_bf16": (_BF16, "ab3efdefb375db1a", 49243.84375 * 2 * 1024, 33280.0 * 1024),
-    "fp8_outlier": (_PIPE, "b950ecf36dbe34db", 189491.90625 * 2 * 1024, 99840.0 * 1024),
+    "fp8_outlier": (_PIPE, "b33c0f454fba9573", 122953.5 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
-    "fp8_blocks_outlier": (_PIPE, "b950ecf36dbe34db", 188260.78125 * 2 * 1024, 99840.0 * 1024),
+    "fp8_blocks_outlier": (_PIPE, "b33c0f454fba9573", 123004.5 * 2 * 1024, 99840.0 * 1024),
     "splitd_bf16_d1024": (_SPLITD8, "dca91d739d485894", 163938.5 * 2 * 1024, 68142.9375 * 1024),
     "splitd_bf16_d768": (_SPLITD, "5de55f883bc0be40", 123050.0 * 2 * 1024, 49280.0 * 1024),
     "splitd_bf16_d512": (_WIDE, "f6d4df4d3cdd1c55", 49594.5 * 2 * 1024, 33408.0 * 1024),
@@ -101,7 +101,7 @@ MEASURED_TRAFFIC = {
     "bwd_causal_bf16": (_BWD, "6e982fcd75cec507", 678817.5 * 2 * 1024, 397390.265625 * 1024),
     "bwd_causal_bf16_d256": (_BWD, "6e982fcd75cec507", 692962.03125 * 2 * 1024, 396023.0625 * 1024),
     "bwd_causal_bf16_d512": (_BWD, "6e982fcd75cec507", 1000050.78125 * 2 * 1024, 446495.171875 * 1024),
-    "prefill_causal_bf16_poly": (_PIPE, "b950ecf36dbe34db", 266960.84375 * 2 * 1024, 133123.546875 * 1024),
+    "prefill_causal_bf16_poly": (_PIPE, "b33c0f454fba9573", 262696.03125 * 2 * 1024, 133120.0 * 1024),
     "fp8_p8_outlier": (_P8, "40c93540ee3a0f74", 169015.1875 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_outlier": (_P8, "40c93540ee3a0f74", 122964.25 * 2 * 1024, 99840.0 * 1024),
     "fp8_lean_causal_32k": (_P8, "40c93540ee3a0f74", 440425.3125 * 2 * 1024, 266244.296875 * 1024),

@@ -10,7 +10,8 @@
 //
 //  * Each wave owns 32 query rows; a work-group of 4 waves owns 128 rows and
 //    two work-groups share a CU, so every SIMD runs two waves from two
-//    independent work-groups.  Their barriers are independent, so while one
+//    independent work-groups (e4m3 D = 128 without the causal mask, on
+//    large grids: one work-group of 8 waves, 256 rows, per CU).  Their barriers are independent, so while one
 //    wave runs its exp/sum/convert work on the vector ALU the other keeps the
 //    matrix pipe busy (the ZYFA article, sections "Why FP8 attention is
 //    softmax-bound on MI355X" and "The three techniques, in plain terms",
@@ -585,6 +586,19 @@ hipError_t launch_pipe(const FwdParams& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// e4m3 D = 128: without the causal mask, and where 256-row work-groups
+// still give every CU one, eight waves share each 64-key tile (half the K
+// loads and V staging per product at the same two waves per SIMD), as in
+// the bf16 kernel of attn_fwd_bf16.hip.
+hipError_t launch_pipe_fp8_d128(const FwdParams& p, hipStream_t stream) {
+  if (!p.causal) {
+    using C8 = PipeCfg<ELT_FP8, 128, 8, 2, 64>;
+    const int64_t wide = (int64_t)p.n_splits * p.B * p.Hq * ((p.Nq + C8::BR - 1) / C8::BR);
+    if (wide >= (int64_t)cu_count()) return launch_pipe<ELT_FP8, 128, 8, 2, 64>(p, stream);
+  }
+  return launch_pipe<ELT_FP8, 128, 4, 2, 64>(p, stream);
+}
+
 }  // namespace
 
 LaunchFn pipe_launcher(int elt, int D) {
@@ -592,7 +606,7 @@ LaunchFn pipe_launcher(int elt, int D) {
     switch (D) {
       // e4m3 K rows of D bytes; V widened to bf16 in LDS
       case 64: return &launch_pipe<ELT_FP8, 64, 4, 2, 64>;
-      case 128: return &launch_pipe<ELT_FP8, 128, 4, 2, 64>;
+      case 128: return &launch_pipe_fp8_d128;
       case 256: return &launch_pipe<ELT_FP8, 256, 4, 2, 32>;
       default: return nullptr;
     }

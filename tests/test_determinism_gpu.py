@@ -82,6 +82,7 @@ def _fp8(case):
 
 FP8 = [
     (1, 24, 24, 1500, 1500, 128, False),
+    (1, 64, 16, 1000, 2000, 128, False),   # eight waves per work-group
     (1, 8, 2, 700, 901, 128, True),
     (1, 4, 2, 500, 600, 256, True),
 ]

@@ -153,6 +153,7 @@ BLOCKS = [
     (1, 2, 2, 1, 70, 128, True),
     (1, 3, 1, 333, 129, 64, True),
     (1, 2, 2, 257, 1000, 128, False),
+    (1, 128, 32, 300, 400, 128, False),     # eight-wave work-groups
 ]
 
 

@@ -147,6 +147,7 @@ CASES = {
     "bf16_d96_tiled": lambda: fwd_case(96, torch.bfloat16, True),
     "f32_d64_tiled": lambda: fwd_case(64, torch.float32, False),
     "fp8_descales": lambda: fp8_case("fp8"),
+    "fp8_descales_8waves": lambda: fp8_case("fp8", causal=False, Hq=256, Hkv=64, Nq=200, Nkv=300),
     "fp8_p_e4m3": lambda: fp8_case("e4m3"),
     "fp8_p_lean": lambda: fp8_case("lean"),
     "exp_poly": poly_case,

@@ -329,6 +329,7 @@ GROWING_FP8 = [
     (1, 2, 2, 200, 300, 64, True, 0.1),
     (1, 2, 2, 100, 110, 256, True, 0.25),
     (1, 2, 1, 150, 300, 256, False, 0.1),
+    (1, 256, 64, 150, 150, 128, False, 0.25),   # eight-wave work-groups
 ]
 
 
@@ -364,6 +365,10 @@ FP8_SMALL = [
     # exact tile multiples and a single element
     (1, 2, 2, 128, 128, 128, True),
     (1, 1, 1, 1, 1, 128, False),
+    # eight waves (256 query rows) per work-group: ragged query and key
+    # tiles, GQA
+    (1, 256, 64, 200, 300, 128, False),
+    (2, 128, 32, 257, 77, 128, False),
 ]
 
 
