@@ -9,9 +9,11 @@
 //
 // Layout (the direct-to-LDS kernel's, attn_fwd_pipe.hip, which keeps the
 // e4m3 paths):
-//  * A work-group is 4 waves x 32 query rows (8 waves, 256 rows, for large
-//    grids without the causal mask); a wave owns its rows through every key
-//    tile.  Transposed products on the 32x32x16 bf16 matrix
+//  * A work-group is 4 waves x 32 query rows of one head; on large grids 8
+//    waves, either 256 rows of one head (no causal mask) or the same 64
+//    rows of 4 query heads that share a KV head (128 rows of 2), so that
+//    every wave sees the same causal key range (GQA).  A wave owns its rows
+//    through every key tile.  Transposed products on the 32x32x16 bf16 matrix
 //    instruction: S^T = K Q^T (A = K from LDS, B = Q held in registers) and
 //    O^T += V^T P^T (A = V^T from the transposing LDS read, B = P).  Lane l
 //    holds query l % 32 in both accumulators, so the S^T registers rounded
@@ -71,10 +73,15 @@ struct Bf16Cfg {
   static_assert(LDS <= 64 * 1024, "two work-groups per CU at least");
 };
 
-template <int D, int BC, int NW = 4>
+template <int D, int BC, int NW = 4, int HP = 1>
 __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : ((D == 128 && BC == 32) ? 3 : 2)) void attn_fwd_bf16_kernel(
     FwdParams p) {
   using C = Bf16Cfg<D, BC, NW>;
+  // HP query heads of one KV head per work-group (GQA), WPH waves each; a
+  // query tile is TR rows of every one of those heads
+  static_assert(NW % HP == 0, "waves must split evenly over the heads");
+  constexpr int WPH = NW / HP;
+  constexpr int TR = WPH * C::QW;
   // LDS: K slot 0, K slot 1, V slot 0, V slot 1
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   const uint32_t lds_base =
@@ -124,13 +131,14 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : ((D == 128 && BC == 32) ? 3 
   for (int job = 0; job < njobs; ++job) {
     // (batch, head) re-derived per job: kept live across the key loop they
     // would take the last registers at three waves per SIMD
-    const int hq = bh % p.Hq;
-    const int b = bh / p.Hq;
+    const int hgroups = p.Hq / HP;
+    const int hq = (bh % hgroups) * HP + wave / WPH;
+    const int b = bh / hgroups;
     const int qt = (p.causal && job == 0) ? (p.n_qtiles - 1 - slot_q) : slot_q;
     if (job > 0) __syncthreads();  // every wave is done with the LDS of the previous tile
     const int hk = hq / p.group;
-    const int q0 = qt * C::BR;
-    const int q0w = q0 + wave * C::QW;
+    const int q0 = qt * TR;
+    const int q0w = q0 + (wave % WPH) * C::QW;
 
     const int64_t q_slab = ((int64_t)b * p.Hq + hq) * (int64_t)p.Nq * D;
     const int64_t kv_slab = (((int64_t)b * p.Hkv + hk) * (int64_t)p.Nkv + kr.k0) * D;
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : ((D == 128 && BC == 32) ? 3 
     const float c = p.scale * kLog2e;  // > 0: the launcher routes other scales elsewhere
 
     int kv_end = kr.nkv;
-    if (p.causal) kv_end = min(kr.nkv, min(q0 + C::BR, p.Nq) + kr.kv_off);
+    if (p.causal) kv_end = min(kr.nkv, min(q0 + TR, p.Nq) + kr.kv_off);
     const int n_kt = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
     auto issue_tile = [&](int t, int slot) {
@@ -320,38 +328,52 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : ((D == 128 && BC == 32) ? 3 
   }  // job
 }
 
-template <int D, int BC, int NW = 4>
+// Work-groups of a launch with NW waves per work-group over HP query heads
+// (query tiles of 32 NW / HP rows), after the causal pairing; fills
+// n_qtiles and pair_causal.
+template <int NW, int HP>
+int64_t bf16_grid(FwdParams& p) {
+  constexpr int TR = NW * 32 / HP;
+  const int64_t heads = (int64_t)p.n_splits * p.B * (p.Hq / HP);
+  p.n_qtiles = (p.Nq + TR - 1) / TR;
+  p.pair_causal = pair_causal_grid(p.causal, heads, p.n_qtiles, p.Nq, p.Nkv);
+  return heads * qtile_slots(p);
+}
+
+template <int D, int BC, int NW = 4, int HP = 1>
 hipError_t launch_bf16(const FwdParams& p0, hipStream_t stream) {
   using C = Bf16Cfg<D, BC, NW>;
   FwdParams p = p0;
-  p.n_qtiles = (p.Nq + C::BR - 1) / C::BR;
-  p.pair_causal = pair_causal_tiles(p);
-  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);
+  if (p.group % HP != 0) return hipErrorInvalidValue;
+  const int64_t total = bf16_grid<NW, HP>(p);
   if (total <= 0 || total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   p.total_wg = (int)total;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BC, NW>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BC, NW, HP>), dim3(p.total_wg), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 // D = 128: 32-key tiles at three waves per SIMD where the grid gives every
 // CU at least three work-groups, otherwise 64-key tiles at two (a grid too
 // small for the third slot gains nothing from the smaller tiles' extra
-// barriers).  Without the causal mask, and where 256-row work-groups still
-// give every CU one, eight waves (256 query rows) share each 64-key K/V
-// tile: half the direct-to-LDS loads and L2-to-LDS bytes per product at
-// two waves per SIMD.  With the mask, a 256-row work-group loads diagonal
-// tiles that its first waves skip, and the four-wave layouts stay faster.
+// barriers).  Where eight-wave work-groups still give every CU one, eight
+// waves share each 64-key K/V tile instead: half the direct-to-LDS loads and
+// L2-to-LDS bytes per product at two waves per SIMD.  Without the causal
+// mask the eight waves take 256 rows of one query head.  With it, a 256-row
+// work-group would load diagonal tiles that its first waves skip, so under
+// GQA the eight waves take the same 64 rows of four query heads of one KV
+// head (128 rows of two for a group of two), which see the same keys;
+// causal MHA keeps the four-wave layouts.
 hipError_t launch_bf16_d128(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;
+  const int64_t cus = cu_count();
   if (!p.causal) {
-    const int64_t wide = (int64_t)p.n_splits * p.B * p.Hq * ((p.Nq + Bf16Cfg<128, 64, 8>::BR - 1) /
-                                                             Bf16Cfg<128, 64, 8>::BR);
-    if (wide >= (int64_t)cu_count()) return launch_bf16<128, 64, 8>(p0, stream);
+    if (bf16_grid<8, 1>(p) >= cus) return launch_bf16<128, 64, 8>(p0, stream);
+  } else if (p.group % 4 == 0) {
+    if (bf16_grid<8, 4>(p) >= cus) return launch_bf16<128, 64, 8, 4>(p0, stream);
+  } else if (p.group % 2 == 0) {
+    if (bf16_grid<8, 2>(p) >= cus) return launch_bf16<128, 64, 8, 2>(p0, stream);
   }
-  p.n_qtiles = (p.Nq + Bf16Cfg<128, 32>::BR - 1) / Bf16Cfg<128, 32>::BR;
-  p.pair_causal = pair_causal_tiles(p);
-  const int64_t total = (int64_t)p.n_splits * p.B * p.Hq * qtile_slots(p);
-  return total >= 3 * (int64_t)cu_count() ? launch_bf16<128, 32>(p0, stream) : launch_bf16<128, 64>(p0, stream);
+  return bf16_grid<4, 1>(p) >= 3 * cus ? launch_bf16<128, 32>(p0, stream) : launch_bf16<128, 64>(p0, stream);
 }
 
 }  // namespace

@@ -47,8 +47,11 @@ def twice(fn):
 BF16 = [
     # (B, Hq, Hkv, Nq, Nkv, D, causal): kernel configuration
     (1, 8, 2, 700, 901, 128, True),      # direct-to-LDS, 64-key tiles (small grid)
-    (1, 64, 16, 2048, 2048, 128, True),  # 32-key tiles, 1024 work-groups, unpaired
-    (2, 64, 16, 4096, 4096, 128, True),  # 32-key tiles, paired causal tiles
+    (1, 64, 64, 2048, 2048, 128, True),  # 32-key tiles, 1024 work-groups, unpaired
+    (2, 64, 64, 4096, 4096, 128, True),  # 32-key tiles, paired causal tiles
+    (1, 64, 16, 2048, 2048, 128, True),  # eight waves over 4 GQA heads, 512 work-groups, unpaired
+    (2, 64, 16, 4096, 4096, 128, True),  # eight waves over 4 GQA heads, paired causal tiles
+    (1, 64, 32, 1500, 1700, 128, True),  # eight waves over 2 GQA heads
     (1, 768, 192, 128, 100, 128, False),  # eight waves, 64-key tiles, one query tile per head
     (1, 64, 16, 1000, 3000, 128, False),  # eight waves, 64-key tiles, 256 work-groups
     (1, 8, 8, 1000, 1000, 64, True),     # direct-to-LDS, D = 64

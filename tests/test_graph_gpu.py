@@ -141,6 +141,7 @@ CASES = {
     "bf16_d128": lambda: fwd_case(128, torch.bfloat16, True),
     "bf16_d64_full": lambda: fwd_case(64, torch.bfloat16, False),
     "bf16_d128_full_8waves": lambda: fwd_case(128, torch.bfloat16, False, Hq=256, Hkv=64, Nq=200, Nkv=300),
+    "bf16_d128_causal_gqa_8waves": lambda: fwd_case(128, torch.bfloat16, True, Hq=256, Hkv=64, Nq=200, Nkv=300),
     "bf16_d512_wide": lambda: fwd_case(512, torch.bfloat16, True, Nq=130, Nkv=150),
     "bf16_d768_splitd": lambda: fwd_case(768, torch.bfloat16, False, Nq=130, Nkv=150),
     "bf16_d1024_splitd8": lambda: fwd_case(1024, torch.bfloat16, True, Nq=130, Nkv=150),

@@ -1,7 +1,8 @@
 """GPU parity on grids large enough for the launchers' large-grid choices:
 causal tiles paired first with last (the ZYFA article, "The details that make
 it production-grade": work-group i of a head runs tiles i and n-1-i), and, for
-bf16 D = 128, 32-key tiles at three waves per SIMD.
+bf16 D = 128, 32-key tiles at three waves per SIMD (MHA) or eight waves over
+the same 64 rows of four query heads (GQA).
 
 The launchers pair only grids that keep at least four work-groups per compute
 unit after pairing, so these shapes are large: 64 query heads of 3850 rows
@@ -57,10 +58,14 @@ def check_lse(L, Lref):
     assert lerr <= TOL_LSE, f"LSE rel err {lerr:.3e}"
 
 
-@pytest.mark.parametrize("D", [128, 64])
-def test_paired_bf16_forward(D):
-    w = Workload("paired", 1, 64, 16, NQ, NKV, D, True, "bf16", seed=21)
-    note(f"bf16 forward, paired causal tiles, Hq=64 Hkv=16 Nq={NQ} Nkv={NKV} D={D}")
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 64, 64), (128, 256, 64), (64, 64, 16)],
+                         ids=["d128_four_waves", "d128_gqa_eight_waves", "d64"])
+def test_paired_bf16_forward(D, Hq, Hkv):
+    """D = 128 MHA: 32-key tiles at three waves per SIMD, 128-row tiles;
+    D = 128 with groups of 4: eight waves over the same 64 rows of 4 query
+    heads (61 tiles, 31 pairs per KV head)."""
+    w = Workload("paired", 1, Hq, Hkv, NQ, NKV, D, True, "bf16", seed=21)
+    note(f"bf16 forward, paired causal tiles, Hq={Hq} Hkv={Hkv} Nq={NQ} Nkv={NKV} D={D}")
     q, k, v = make_inputs(w)
     O, L = A.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=w.scale)
     torch.cuda.synchronize()
@@ -69,7 +74,7 @@ def test_paired_bf16_forward(D):
     assert np.isfinite(O).all()
     G = w.Hq // w.Hkv
     worst = 0.0
-    for h in HEADS:
+    for h in (0, Hq // 2 - 1, Hq - 1):
         qkv = [t[0, x].to(torch.float64).numpy() for t, x in ((q, h), (k, h // G), (v, h // G))]
         Oref, Lref = oracle.attention_head(*qkv, w.scale, True)
         worst = max(worst, check_bf16(O[0, h], L[0, h], Oref, Lref, h, qkv, w.scale, True))

@@ -127,10 +127,17 @@ SMALL = [
     (1, 2, 2, 513, 1500, 128, False, "bf16"),
     # grids of 768 work-groups over few keys, so each key tile carries a
     # large share of every row: causal, 32-key tiles at three waves per SIMD
-    # (keyless rows, a ragged last tile, MHA and GQA); without the mask,
-    # eight waves (256 query rows) per work-group and 64-key tiles
+    # (keyless rows, a ragged last tile, MHA and a GQA group of 3); causal
+    # GQA with an even group, eight waves over 4 (2) query heads of one KV
+    # head; without the mask, eight waves (256 query rows) per work-group
+    # and 64-key tiles
     (1, 768, 768, 128, 77, 128, True, "bf16"),
+    (1, 768, 256, 100, 100, 128, True, "bf16"),
     (1, 768, 192, 100, 100, 128, True, "bf16"),
+    (1, 1024, 256, 100, 77, 128, True, "bf16"),
+    (1, 512, 256, 130, 300, 128, True, "bf16"),
+    (1, 2048, 256, 64, 200, 128, True, "bf16"),
+    (2, 256, 64, 200, 333, 128, True, "bf16"),
     (1, 768, 192, 128, 77, 128, False, "bf16"),
     (1, 768, 768, 100, 100, 128, False, "bf16"),
     # eight-wave work-groups: ragged 256-row query tiles and 64-key tiles,

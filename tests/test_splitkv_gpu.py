@@ -126,6 +126,7 @@ SPLITKV = [
     (1, 2, 2, 100, 1200, 128, False, "fp8", 6),
     (1, 2, 2, 120, 100, 128, True, "bf16", 1),          # Nq > Nkv: keyless rows, one split
     (1, 32, 8, 300, 4000, 128, False, "bf16", 8),       # 512 eight-wave work-groups over the ranges
+    (1, 32, 8, 300, 4000, 128, True, "bf16", 8),        # causal: eight waves over 4 GQA heads per range
     (1, 32, 8, 300, 4000, 128, False, "fp8", 8),
 ]
 
