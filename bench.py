@@ -84,9 +84,9 @@ _WIDE = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_fwd_wide.hip")
 _BWD = ("attn_common.h", "attn_dma.h", "attn_launch.h", "attn_bwd.h", "attn_bwd.hip")
 MEASURED_TRAFFIC = {
     # workload: (kernel sources, source hash, bytes read, bytes written)
-    "prefill_causal_bf16": (_BF16, "ab3efdefb375db1a", 281431.3125 * 2 * 1024, 137430.453125 * 1024),
-    "gqa_causal_bf16": (_BF16, "ab3efdefb375db1a", 200251.21875 * 2 * 1024, 137226.421875 * 1024),
-    "gqa_cross_bf16": (_BF16, "ab3efdefb375db1a", 49243.84375 * 2 * 1024, 33280.0 * 1024),
+    "prefill_causal_bf16": (_BF16, "233822d0f6f3ebb5", 281102.375 * 2 * 1024, 137414.96875 * 1024),
+    "gqa_causal_bf16": (_BF16, "233822d0f6f3ebb5", 144185.4375 * 2 * 1024, 133120.0 * 1024),
+    "gqa_cross_bf16": (_BF16, "233822d0f6f3ebb5", 49249.25 * 2 * 1024, 33280.0 * 1024),
     "fp8_outlier": (_PIPE, "b33c0f454fba9573", 122953.5 * 2 * 1024, 99840.0 * 1024),
     # the attention launch of the fp8 input pipeline (the quantisers read and
     # write each byte once)
@@ -96,7 +96,7 @@ MEASURED_TRAFFIC = {
     "splitd_bf16_d512": (_WIDE, "f6d4df4d3cdd1c55", 49594.5 * 2 * 1024, 33408.0 * 1024),
     # the partial-attention launch over 8 key ranges (the merge launch after
     # it reads and writes its parts once)
-    "chunk_prefill_splitkv_bf16": (_BF16, "ab3efdefb375db1a", 73826.71875 * 2 * 1024, 33024.0 * 1024),
+    "chunk_prefill_splitkv_bf16": (_BF16, "233822d0f6f3ebb5", 73820.5625 * 2 * 1024, 33088.25 * 1024),
     # the whole backward step: prep + dK/dV + dQ launches
     "bwd_causal_bf16": (_BWD, "6e982fcd75cec507", 678817.5 * 2 * 1024, 397390.265625 * 1024),
     "bwd_causal_bf16_d256": (_BWD, "6e982fcd75cec507", 692962.03125 * 2 * 1024, 396023.0625 * 1024),
